@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: forward + backward of a row-wise normalization layer on one MI355X.
+
+A step is one forward and one backward (stage 1 + stage 2) of the layer over one batch of
+synthetic input already resident in HBM.  Several copies of the inputs rotate through the
+timed steps so that every step reads data last touched more than ~768 MB earlier, past the
+256 MB Infinity Cache: the rate is HBM bandwidth, not cache bandwidth.
+
+Prints ONE JSON line: value = algorithmic fwd+bwd bytes per step / step time (GB/s), a
+roofline object for the dominant kernel (its algorithmic bytes / its average duration, timed
+with HIP events around each launch in the timed region), and the CPU oracle timed on a bounded
+row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+METRIC = "achieved HBM GB/s (fwd+bwd) and % of peak, M>>N and wide-row norm configs"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
+    ap.add_argument("--sweep", default=None, help="also time every workload and write JSON lines here")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    d = os.path.join(ROOT, "row_wise_normalization_dyt_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(wl, kernel: str) -> int:
+    """Algorithmic HBM bytes of one launch of `kernel` on workload wl."""
+    sx = 4 if wl.xdt == "f32" else 2
+    sp = 4 if wl.pdt == "f32" else 2
+    e = wl.M * wl.N
+    stats = {"dyt": 0, "layernorm": 8, "rmsnorm": 4}[wl.layer] * wl.M
+    nvec = {"dyt": 2, "layernorm": 2, "rmsnorm": 1}[wl.layer]
+    if kernel.endswith("_fwd"):
+        return 2 * e * sx + stats + nvec * wl.N * sp + (sp if wl.layer == "dyt" else 0)
+    if kernel.endswith("_bwd"):
+        return 3 * e * sx + stats + wl.N * sp + (sp if wl.layer == "dyt" else 0)
+    if kernel == "colreduce":
+        return nvec * wl.N * sp + (sp if wl.layer == "dyt" else 0)
+    return 0
+
+
+def time_workload(wl, steps: int, warmup: int):
+    import torch
+    import workloads
+    import row_wise_normalization_dyt_amd as rwn
+    from row_wise_normalization_dyt_amd.prepared import PreparedStep
+
+    base = workloads.make_inputs(wl, "cuda")
+    sx = 4 if wl.xdt == "f32" else 2
+    set_bytes = 4 * wl.M * wl.N * sx + 16 * wl.M
+    nsets = max(1, min(256, math.ceil(3 * MALL_BYTES / max(set_bytes, 1))))
+    sets = []
+    for i in range(nsets):
+        inp = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        sets.append(PreparedStep(wl.layer, inp, wl.eps))
+    for i in range(warmup):
+        sets[i % nsets].step()
+    torch.cuda.synchronize()
+
+    rwn.trace_begin(3 * steps + 8)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        sets[i % nsets].step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    trace = rwn.trace_end(3 * steps + 8)
+    ms_total = t0.elapsed_time(t1)
+    per = {}
+    for name, ms in trace:
+        tot, cnt = per.get(name, (0.0, 0))
+        per[name] = (tot + ms, cnt + 1)
+    kernels = {k: {"avg_ms": t / c, "launches": c, "total_ms": t} for k, (t, c) in per.items()}
+    return {"ms_per_step": ms_total / steps, "wall_s": wall, "kernels": kernels, "nsets": nsets,
+            "outputs": sets[0].outputs(), "inputs": base}
+
+
+def roofline(wl, kernels, traffic_db):
+    dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
+    b = kernel_bytes(wl, dom)
+    achieved = b / (kernels[dom]["avg_ms"] * 1e-3) / 1e9
+    traffic = None
+    rec = traffic_db.get(f"{wl.name}/{dom}")
+    if rec and rec.get("kernel_source_sha") == kernel_source_sha():
+        traffic = rec.get("hbm_bytes_per_launch")
+    return {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": b, "avg_launch_ms": round(kernels[dom]["avg_ms"], 5)}
+
+
+def cpu_baseline(wl, inputs, target_s: float):
+    """The oracle (as it stands) on rows [0, S) of the same workload, S sized for ~target_s."""
+    import oracle
+    import workloads
+    h = {k: v.detach().cpu() for k, v in inputs.items()}
+
+    def run(S):
+        sub = {k: (v[:S] if k in ("x", "dy") else v) for k, v in h.items()}
+        e = workloads.eps_f32(wl.eps)
+        t = time.perf_counter()
+        if wl.layer == "dyt":
+            oracle.dyt_fwd(sub["x"], sub["alpha"], sub["gamma"], sub["beta"])
+            oracle.dyt_bwd(sub["x"], sub["dy"], sub["alpha"], sub["gamma"])
+        elif wl.layer == "layernorm":
+            oracle.layernorm_fwd(sub["x"], sub["gamma"], sub["beta"], e)
+            oracle.layernorm_bwd(sub["x"], sub["dy"], sub["gamma"], e)
+        else:
+            oracle.rmsnorm_fwd(sub["x"], sub["weight"], e)
+            oracle.rmsnorm_bwd(sub["x"], sub["dy"], sub["weight"], e)
+        return time.perf_counter() - t
+
+    S0 = max(1, min(wl.M, 2_000_000 // wl.N))
+    t0 = run(S0)
+    S = max(1, min(wl.M, int(S0 * target_s / max(t0, 1e-3))))
+    t = run(S) if S != S0 else t0
+    sub_wl = wl.with_(M=S)
+    gbps = sub_wl.algorithmic_bytes()["total"] / t / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"rows [0, {S}) of {wl.M} x {wl.N} ({S * wl.N} elements), fwd+bwd, {t:.1f} s"}
+
+
+def copy_probe_gbps():
+    import torch
+    import row_wise_normalization_dyt_amd as rwn
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        rwn.copy_probe(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(10):
+        rwn.copy_probe(a, b) if i % 2 == 0 else rwn.copy_probe(b, a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the path shards across GPUs by rows "
+              "(see the design notes), but no multi-GPU run is part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    torch.cuda.set_device(0)
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    tdb_path = os.path.join(ROOT, "profiles", "traffic.json")
+    traffic_db = json.load(open(tdb_path)) if os.path.exists(tdb_path) else {}
+
+    r = time_workload(wl, args.steps, args.warmup)
+    byts = wl.algorithmic_bytes()["total"]
+    value = byts / (r["ms_per_step"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.xdt, "data": "synthetic",
+        "config": {"workload": wl.name, "layer": wl.layer, "M": wl.M, "N": wl.N, "x_dtype": wl.xdt,
+                   "param_dtype": wl.pdt, "bytes_per_step": byts,
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "rotating_input_sets": r["nsets"],
+                   "kernel_avg_ms": {k: round(v["avg_ms"], 5) for k, v in r["kernels"].items()},
+                   "copy_probe_GBps": copy_probe_gbps()},
+        "roofline": roofline(wl, r["kernels"], traffic_db),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, r["inputs"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for n, w in workloads.WORKLOADS.items():
+                del r
+                torch.cuda.empty_cache()
+                r = time_workload(w, max(10, min(args.steps, 100)), 5)
+                b = w.algorithmic_bytes()
+                v = b["total"] / (r["ms_per_step"] * 1e-3) / 1e9
+                rec = {"workload": n, "GBps": round(v, 1), "pct_of_peak": round(100 * v / HBM_PEAK_GBPS, 2),
+                       "ms_per_step": round(r["ms_per_step"], 5), "bytes_per_step": b["total"],
+                       "kernels": {k: round(x["avg_ms"], 5) for k, x in r["kernels"].items()},
+                       "roofline": roofline(w, r["kernels"], traffic_db)}
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print("sweep", json.dumps(rec), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * rwnorm.h -- C ABI of librwnorm: forward and backward of three row-wise per-channel
+ * normalization layers over a row-major [M, N] activation matrix on an AMD Instinct MI355X
+ * (gfx950), with hand-written HIP kernels.
+ *
+ * Layers (each entry point cites the passage that defines it):
+ *   DyT        y = gamma * tanh(alpha * x) + beta, scalar alpha
+ *              (Liger-Kernel PR #1617 "fix(dyt): use a 1D grid and tile small-width rows", Summary)
+ *   LayerNorm  y = (x - mean) * rstd * gamma + beta, biased variance, eps inside the square root
+ *              (intel/torch-xpu-ops PR #1880 "Layernorm bwd OPT", description; torch.nn.LayerNorm)
+ *   RMSNorm    y = weight * (x.float() * rsqrt(mean(x.float()^2) + eps)).to(x.dtype)
+ *              (DeepSpeed PR #8645 / #8664, Summary and Semantics)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout     x, dy, y, dx are row-major contiguous [M, N] (row pitch N elements).  Any
+ *            element-aligned address is accepted, but x, dy, y and dx of one call must share
+ *            the same address modulo 16 bytes (fresh allocations always do).  Parameters are
+ *            contiguous [N] vectors; alpha is a one-element device buffer; statistics are
+ *            float32 [M].
+ * Dtypes     x, dy, y, dx use x_dtype.  The parameters (alpha, gamma, beta, weight) and their
+ *            gradients use param_dtype.  Supported pairs (x_dtype, param_dtype): (F32, F32),
+ *            (BF16, F32), (BF16, BF16).  Arithmetic is float32; outputs are rounded once
+ *            (round to nearest even) to their dtype, except for the RMSNorm rounding points.
+ * Ownership  Every pointer is device memory owned by the caller.  The library never allocates,
+ *            frees or synchronizes on these calls; work is enqueued on `stream` (a hipStream_t,
+ *            NULL = the default stream) and the call returns after launch.
+ * Errors     Invalid arguments are reported before anything is launched or written, with a
+ *            message available from rwn_last_error() (thread-local).  No C++ exception crosses
+ *            this boundary.
+ * Empty M    M == 0 is valid: a forward writes nothing; a backward writes zeros to every
+ *            requested parameter gradient (the sum over no rows).
+ * Backward   Parameter gradients are column sums over all M rows, computed by a two-stage,
+ *            atomic-free reduction: per-workgroup float32 partial rows in the caller's workspace,
+ *            then a fixed-order float64 pass over them.  Results are bitwise reproducible run
+ *            to run for the same inputs, device and library build.  A NULL gradient pointer
+ *            skips writing that gradient.
+ * Gradients  First-order only; eps is a constant.
+ * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16
+ *            elements) spread over at most 1024 threads; when N is not a multiple of the chunk
+ *            or the operands are not 16-byte aligned a row may straddle one more chunk, so
+ *            those calls take N <= 16381 (float32) / 16377 (bfloat16) and otherwise return
+ *            RWN_ERR_UNSUPPORTED.
+ */
+#ifndef RWNORM_H
+#define RWNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RWN_F32 = 0, RWN_BF16 = 1 } rwn_dtype;
+
+typedef enum {
+    RWN_OK = 0,
+    RWN_ERR_INVALID_ARG = 1,  /* negative M, N < 1, NULL required pointer, bad eps, bad dtype code */
+    RWN_ERR_UNSUPPORTED = 2,  /* valid but unsupported: dtype pair, mismatched 16-byte alignment */
+    RWN_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace_size query */
+    RWN_ERR_LAUNCH = 4,       /* a HIP launch or device query failed (message names the HIP error) */
+} rwn_status;
+
+/* ---------------------------------------------------------------------------------- DyT */
+
+/* Forward (Liger-Kernel PR #1617, Summary): y_ij = gamma_j * tanh(alpha * x_ij) + beta_j.
+ * alpha: device [1]; gamma, beta: device [N]; y: device [M, N] in x_dtype.  With alpha = +inf
+ * an element x = 0 gives tanh(inf * 0) = NaN, as in exact arithmetic. */
+rwn_status dyt_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype, const void* alpha,
+                   const void* gamma, const void* beta, rwn_dtype param_dtype, void* y,
+                   void* stream);
+
+/* Backward (same passage): with t = tanh(alpha x), s = sech^2(alpha x):
+ *   dx = dy * gamma * alpha * s, where alpha * s is taken as 0 when s == 0 (so alpha = +inf
+ *        gives dx = 0 instead of inf * 0),
+ *   dgamma_j = sum_i dy*t,  dbeta_j = sum_i dy,  dalpha = sum_ij dy*gamma*x*s.
+ * Rows beyond M inside a tile are masked after the arithmetic, so they cannot inject NaN.
+ * dx: [M, N] x_dtype.  dalpha [1], dgamma [N], dbeta [N] in param_dtype (each may be NULL).
+ * workspace: device buffer of at least dyt_bwd_workspace_size() bytes, any content. */
+rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, rwn_dtype x_dtype,
+                   const void* alpha, const void* gamma, rwn_dtype param_dtype, void* dx,
+                   void* dalpha, void* dgamma, void* dbeta, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes dyt_bwd needs for (M, N, x_dtype) on the current HIP device. */
+rwn_status dyt_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes);
+
+/* ---------------------------------------------------------------------------- LayerNorm */
+
+/* Forward (intel/torch-xpu-ops PR #1880, description; torch.nn.LayerNorm semantics):
+ *   mean = sum_j x / N,  var = sum_j (x - mean)^2 / N,  rstd = 1 / sqrt(var + eps),
+ *   y = (x - mean) * rstd * gamma + beta.
+ * eps: finite, >= 0, used as the float32 value given.  mean, rstd: device float32 [M], each
+ * may be NULL (not written). */
+rwn_status layernorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                         const void* gamma, const void* beta, rwn_dtype param_dtype, float eps,
+                         void* y, float* mean, float* rstd, void* stream);
+
+/* Backward (same passage: the dgamma/dbeta column reduction that dominates when M >> N).
+ * With xhat = (x - mean) * rstd, g = dy * gamma, c1 = mean_j g, c2 = mean_j g * xhat:
+ *   dx = rstd * (g - c1 - xhat * c2),  dgamma_j = sum_i dy * xhat,  dbeta_j = sum_i dy.
+ * mean/rstd: the forward's statistics; pass both NULL to recompute them from x with eps.
+ * dgamma, dbeta: [N] param_dtype, each may be NULL. */
+rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, rwn_dtype x_dtype,
+                         const float* mean, const float* rstd, const void* gamma,
+                         rwn_dtype param_dtype, float eps, void* dx, void* dgamma, void* dbeta,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes);
+
+/* ------------------------------------------------------------------------------ RMSNorm */
+
+/* Forward (DeepSpeed PR #8645, Summary and Semantics): float32 statistics
+ *   rstd = 1 / sqrt(sum_j x^2 / N + eps),  n = round_x_dtype(x * rstd),
+ *   y = round_x_dtype(float32(weight * n)).
+ * y keeps x_dtype also for a float32 weight.  rstd: device float32 [M] or NULL. */
+rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype, const void* weight,
+                       rwn_dtype weight_dtype, float eps, void* y, float* rstd, void* stream);
+
+/* Backward (same passage): g = round_x_dtype(float32(dy * weight)), h = x * rstd (unrounded),
+ *   c = mean_j g * h,  dx = rstd * (g - h * c),
+ *   dweight_j = sum_i round_weight_dtype(float32(dy * n)), n = round_x_dtype(h).
+ * rstd: the forward's statistic, or NULL to recompute it from x with eps.  dweight may be
+ * NULL. */
+rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, rwn_dtype x_dtype,
+                       const float* rstd, const void* weight, rwn_dtype weight_dtype, float eps,
+                       void* dx, void* dweight, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+rwn_status rmsnorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes);
+
+/* ------------------------------------------------------------------------------ support */
+
+/* Message of the last failed call on this thread ("" after a successful call). */
+const char* rwn_last_error(void);
+
+/* Library version string. */
+const char* rwn_version(void);
+
+/* Kernel-duration trace, a measurement aid.  After rwn_trace_begin(capacity) every kernel the
+ * entry points launch on this thread is bracketed by a pair of HIP events on its stream (up
+ * to `capacity` kernels; the library creates the events here).  rwn_trace_end() waits for
+ * the recorded events, writes up to `capacity` durations in milliseconds and kernel tags
+ * (see rwn_kernel_tag), releases the events and returns the number of entries, or -1 on a HIP
+ * error.  Tracing is off until rwn_trace_begin is called. */
+typedef enum {
+    RWN_K_DYT_FWD = 1, RWN_K_DYT_BWD = 2, RWN_K_LN_FWD = 3, RWN_K_LN_BWD = 4,
+    RWN_K_RMS_FWD = 5, RWN_K_RMS_BWD = 6, RWN_K_COLREDUCE = 7, RWN_K_COPY = 8
+} rwn_kernel_tag;
+rwn_status rwn_trace_begin(int capacity);
+int rwn_trace_end(float* ms, int* tags, int capacity);
+
+/* Bandwidth probe, a measurement aid: copies `bytes` from src to dst with 16-byte vector
+ * loads and stores (both 16-byte aligned, bytes a multiple of 16), enqueued on `stream`. */
+rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Launch plan the library chooses for an entry point (introspection for tests and tuning).
+ * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 9 integers to out:
+ * {mode (0 aligned vectors, 1 shifted vectors, 2 scalar), chunks per thread, rows per thread,
+ *  threads per row, row slots per workgroup, workgroup size, workgroups, row tiles,
+ *  elements per chunk}.  misalign_bytes is the common address of x/y/dy/dx modulo 16; cus is
+ * the compute-unit count to plan for (0: query the current device). */
+rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
+                    int misalign_bytes, int cus, int64_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWNORM_H */

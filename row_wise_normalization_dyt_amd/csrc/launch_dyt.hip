@@ -1,0 +1,41 @@
+// DyT launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT).
+#include "rwn_kernels.hpp"
+#include "rwn_launch.hpp"
+
+namespace rwn {
+
+hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                          const void* gamma, const void* beta, void* y, hipStream_t s) {
+    const Geom g = make_geom(p);
+    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+            hipLaunchKernelGGL((dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>),
+                               dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
+                               (const PT*)alpha, (const PT*)gamma, (const PT*)beta, (T*)y, g);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                          const void* alpha, const void* gamma, void* dx, float* ws,
+                          hipStream_t s) {
+    const Geom g = make_geom(p);
+    const int64_t ng = partial_cols(LAYER_DYT, p.N);
+    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+            hipLaunchKernelGGL((dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>),
+                               dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
+                               (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, ng, g);
+            return hipGetLastError();
+        });
+    });
+}
+
+}  // namespace rwn

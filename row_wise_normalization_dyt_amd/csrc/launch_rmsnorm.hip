@@ -1,0 +1,41 @@
+// RMSNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT).
+#include "rwn_kernels.hpp"
+#include "rwn_launch.hpp"
+
+namespace rwn {
+
+hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* w,
+                          float eps, void* y, float* rstd, hipStream_t s) {
+    const Geom g = make_geom(p);
+    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+            hipLaunchKernelGGL((rms_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>),
+                               dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
+                               (const PT*)w, eps, (T*)y, rstd, g);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                          const float* rstd, const void* w, float eps, void* dx, float* ws,
+                          hipStream_t s) {
+    const Geom g = make_geom(p);
+    const int64_t ng = partial_cols(LAYER_RMS, p.N);
+    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+            hipLaunchKernelGGL((rms_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>),
+                               dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
+                               (const T*)dy, rstd, (const PT*)w, eps, (T*)dx, ws, ng, g);
+            return hipGetLastError();
+        });
+    });
+}
+
+}  // namespace rwn

@@ -1,0 +1,460 @@
+// C ABI of librwnorm: argument validation, launch planning and kernel-duration tracing.
+// Declarations and the contract of each entry point are in include/rwnorm.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "../../include/rwnorm.h"
+#include "rwn_launch.hpp"
+
+#define RWN_API extern "C" __attribute__((visibility("default")))
+
+using namespace rwn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rwn_status ok() {
+    g_err[0] = '\0';
+    return RWN_OK;
+}
+
+rwn_status fail(rwn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rwn_status hip_fail(hipError_t e, const char* what) {
+    return fail(RWN_ERR_LAUNCH, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// Compute units of the current device, cached per device.
+rwn_status device_cus(int* cus) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev >= 0 && dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) {
+            *cus = v;
+            return RWN_OK;
+        }
+    }
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    if (v <= 0) return fail(RWN_ERR_LAUNCH, "device reports %d compute units", v);
+    if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    *cus = v;
+    return RWN_OK;
+}
+
+rwn_status check_shape_dtypes(const char* fn, int64_t M, int64_t N, rwn_dtype xdt, rwn_dtype pdt) {
+    if (M < 0) return fail(RWN_ERR_INVALID_ARG, "%s: M must be >= 0 (got %lld)", fn, (long long)M);
+    if (N < 1) return fail(RWN_ERR_INVALID_ARG, "%s: N must be >= 1 (got %lld)", fn, (long long)N);
+    if ((int)xdt != RWN_F32 && (int)xdt != RWN_BF16)
+        return fail(RWN_ERR_INVALID_ARG, "%s: unknown x dtype code %d", fn, (int)xdt);
+    if ((int)pdt != RWN_F32 && (int)pdt != RWN_BF16)
+        return fail(RWN_ERR_INVALID_ARG, "%s: unknown parameter dtype code %d", fn, (int)pdt);
+    if (xdt == RWN_F32 && pdt == RWN_BF16)
+        return fail(RWN_ERR_UNSUPPORTED, "%s: float32 x with bfloat16 parameters is not supported", fn);
+    if (N > kMaxN)
+        return fail(RWN_ERR_UNSUPPORTED, "%s: N = %lld is wider than the supported %lld", fn,
+                    (long long)N, (long long)kMaxN);
+    if (M > 0 && N > INT64_MAX / M)
+        return fail(RWN_ERR_INVALID_ARG, "%s: M * N overflows", fn);
+    return RWN_OK;
+}
+
+rwn_status check_eps(const char* fn, float eps) {
+    if (!(eps >= 0.0f) || isinf(eps))
+        return fail(RWN_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+    return RWN_OK;
+}
+
+// The [M, N] operands must be element aligned and share their address modulo 16.
+rwn_status check_operands(const char* fn, rwn_dtype xdt, const void* const* ptrs,
+                          const char* const* names, int n, int* misalign) {
+    const uintptr_t esz = xdt == RWN_F32 ? 4 : 2;
+    int m = -1;
+    for (int i = 0; i < n; ++i) {
+        if (!ptrs[i]) return fail(RWN_ERR_INVALID_ARG, "%s: %s is NULL", fn, names[i]);
+        const uintptr_t a = (uintptr_t)ptrs[i];
+        if (a % esz) return fail(RWN_ERR_INVALID_ARG, "%s: %s is not aligned to its element size", fn, names[i]);
+        const int mm = (int)(a % 16);
+        if (m < 0) m = mm;
+        else if (mm != m)
+            return fail(RWN_ERR_UNSUPPORTED,
+                        "%s: %s does not share the address modulo 16 of %s (%d vs %d); pass freshly "
+                        "allocated or equally offset buffers", fn, names[i], names[0], mm, m);
+    }
+    *misalign = m < 0 ? 0 : m;
+    return RWN_OK;
+}
+
+// --------------------------------------------------------------------------- tracing
+
+struct TraceEntry {
+    int tag;
+    hipEvent_t a, b;
+};
+
+struct Trace {
+    bool on = false;
+    int cap = 0;
+    int used = 0;
+    std::vector<TraceEntry> ev;
+};
+
+thread_local Trace g_trace;
+
+template <typename F>
+hipError_t traced(int tag, hipStream_t s, F&& launch) {
+    Trace& t = g_trace;
+    if (!t.on || t.used >= t.cap) return launch();
+    TraceEntry& e = t.ev[t.used];
+    hipError_t r = hipEventRecord(e.a, s);
+    if (r != hipSuccess) return r;
+    r = launch();
+    if (r != hipSuccess) return r;
+    r = hipEventRecord(e.b, s);
+    if (r != hipSuccess) return r;
+    e.tag = tag;
+    ++t.used;
+    return hipSuccess;
+}
+
+rwn_status plan_for(const char* fn, int layer, bool bwd, int64_t M, int64_t N, rwn_dtype xdt,
+                    int misalign, Plan* p) {
+    int cus = 0;
+    rwn_status st = device_cus(&cus);
+    if (st != RWN_OK) return st;
+    if (!make_plan(layer, bwd, M, N, (int)xdt, misalign, cus, p))
+        return fail(RWN_ERR_UNSUPPORTED,
+                    "%s: N = %lld with operands %d bytes past a 16-byte boundary needs more than "
+                    "1024 threads per row; use 16-byte-aligned operands and N a multiple of %d",
+                    fn, (long long)N, misalign, xdt == RWN_F32 ? 4 : 8);
+    return RWN_OK;
+}
+
+rwn_status workspace_size(int layer, int64_t M, int64_t N, rwn_dtype xdt, size_t* bytes) {
+    const char* fn = layer == LAYER_DYT ? "dyt_bwd_workspace_size"
+                     : layer == LAYER_LN ? "layernorm_bwd_workspace_size"
+                                         : "rmsnorm_bwd_workspace_size";
+    if (!bytes) return fail(RWN_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+    rwn_status st = check_shape_dtypes(fn, M, N, xdt, RWN_F32);
+    if (st != RWN_OK) return st;
+    if (M == 0) {
+        *bytes = 0;
+        return ok();
+    }
+    // The plan depends on the operands' address modulo 16; size for the largest.
+    const int esz = xdt == RWN_F32 ? 4 : 2;
+    int64_t grid = 0;
+    for (int mis = 0; mis < 16; mis += esz) {
+        Plan p;
+        st = plan_for(fn, layer, true, M, N, xdt, mis, &p);
+        if (st != RWN_OK) return st;
+        if (p.grid > grid) grid = p.grid;
+    }
+    *bytes = (size_t)grid * (size_t)partial_cols(layer, N) * sizeof(float);
+    return ok();
+}
+
+rwn_status check_workspace(const char* fn, const Plan& p, int layer, const void* ws, size_t ws_bytes) {
+    const size_t need = (size_t)p.grid * (size_t)partial_cols(layer, p.N) * sizeof(float);
+    if (need == 0) return RWN_OK;
+    if (!ws) return fail(RWN_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (ws_bytes < need)
+        return fail(RWN_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, ws_bytes, need);
+    if ((uintptr_t)ws % 4) return fail(RWN_ERR_INVALID_ARG, "%s: workspace is not 4-byte aligned", fn);
+    return RWN_OK;
+}
+
+// Stage 2 (also the whole backward when M == 0: P = 0 partial rows give zeros).
+rwn_status finish_bwd(const char* fn, int pdt, const float* ws, int64_t P, int64_t ng, int64_t N,
+                      void* out0, void* out1, void* out2, hipStream_t s) {
+    if (!out0 && !out1 && !out2) return ok();
+    hipError_t e = traced(RWN_K_COLREDUCE, s, [&] {
+        return launch_colreduce(pdt, ws, P, ng, N, out0, out1, out2, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+}  // namespace
+
+// ====================================================================================== DyT
+
+RWN_API rwn_status dyt_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                           const void* alpha, const void* gamma, const void* beta,
+                           rwn_dtype param_dtype, void* y, void* stream) {
+    const char* fn = "dyt_fwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, param_dtype);
+    if (st != RWN_OK) return st;
+    if (!alpha || !gamma || !beta) return fail(RWN_ERR_INVALID_ARG, "%s: alpha, gamma and beta are required", fn);
+    if (M == 0) return ok();
+    const void* ops[2] = {x, y};
+    const char* names[2] = {"x", "y"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 2, &mis)) != RWN_OK) return st;
+    Plan p;
+    if ((st = plan_for(fn, LAYER_DYT, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = traced(RWN_K_DYT_FWD, s, [&] {
+        return launch_dyt_fwd(p, x_dtype, param_dtype, x, alpha, gamma, beta, y, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+RWN_API rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, rwn_dtype x_dtype,
+                           const void* alpha, const void* gamma, rwn_dtype param_dtype, void* dx,
+                           void* dalpha, void* dgamma, void* dbeta, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const char* fn = "dyt_bwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, param_dtype);
+    if (st != RWN_OK) return st;
+    if (!alpha || !gamma) return fail(RWN_ERR_INVALID_ARG, "%s: alpha and gamma are required", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ng = partial_cols(LAYER_DYT, N);
+    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, N, dgamma, dbeta, dalpha, s);
+    const void* ops[3] = {x, dy, dx};
+    const char* names[3] = {"x", "dy", "dx"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
+    Plan p;
+    if ((st = plan_for(fn, LAYER_DYT, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = check_workspace(fn, p, LAYER_DYT, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = (float*)workspace;
+    hipError_t e = traced(RWN_K_DYT_BWD, s, [&] {
+        return launch_dyt_bwd(p, x_dtype, param_dtype, x, dy, alpha, gamma, dx, ws, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return finish_bwd(fn, param_dtype, ws, p.grid, ng, N, dgamma, dbeta, dalpha, s);
+}
+
+RWN_API rwn_status dyt_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
+    return workspace_size(LAYER_DYT, M, N, x_dtype, bytes);
+}
+
+// ================================================================================ LayerNorm
+
+RWN_API rwn_status layernorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                                 const void* gamma, const void* beta, rwn_dtype param_dtype,
+                                 float eps, void* y, float* mean, float* rstd, void* stream) {
+    const char* fn = "layernorm_fwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, param_dtype);
+    if (st != RWN_OK) return st;
+    if ((st = check_eps(fn, eps)) != RWN_OK) return st;
+    if (M == 0) return ok();
+    const void* ops[2] = {x, y};
+    const char* names[2] = {"x", "y"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 2, &mis)) != RWN_OK) return st;
+    if (((uintptr_t)mean % 4) || ((uintptr_t)rstd % 4))
+        return fail(RWN_ERR_INVALID_ARG, "%s: mean/rstd must be float aligned", fn);
+    Plan p;
+    if ((st = plan_for(fn, LAYER_LN, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = traced(RWN_K_LN_FWD, s, [&] {
+        return launch_ln_fwd(p, x_dtype, param_dtype, x, gamma, beta, eps, y, mean, rstd, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
+                                 rwn_dtype x_dtype, const float* mean, const float* rstd,
+                                 const void* gamma, rwn_dtype param_dtype, float eps, void* dx,
+                                 void* dgamma, void* dbeta, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    const char* fn = "layernorm_bwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, param_dtype);
+    if (st != RWN_OK) return st;
+    if ((st = check_eps(fn, eps)) != RWN_OK) return st;
+    if ((mean == nullptr) != (rstd == nullptr))
+        return fail(RWN_ERR_INVALID_ARG, "%s: pass both mean and rstd, or neither", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ng = partial_cols(LAYER_LN, N);
+    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, N, dgamma, dbeta, nullptr, s);
+    const void* ops[3] = {x, dy, dx};
+    const char* names[3] = {"x", "dy", "dx"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
+    Plan p;
+    if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = (float*)workspace;
+    hipError_t e = traced(RWN_K_LN_BWD, s, [&] {
+        return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return finish_bwd(fn, param_dtype, ws, p.grid, ng, N, dgamma, dbeta, nullptr, s);
+}
+
+RWN_API rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
+    return workspace_size(LAYER_LN, M, N, x_dtype, bytes);
+}
+
+// ================================================================================== RMSNorm
+
+RWN_API rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                               const void* weight, rwn_dtype weight_dtype, float eps, void* y,
+                               float* rstd, void* stream) {
+    const char* fn = "rmsnorm_fwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, weight_dtype);
+    if (st != RWN_OK) return st;
+    if ((st = check_eps(fn, eps)) != RWN_OK) return st;
+    if (!weight) return fail(RWN_ERR_INVALID_ARG, "%s: weight is required", fn);
+    if (M == 0) return ok();
+    const void* ops[2] = {x, y};
+    const char* names[2] = {"x", "y"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 2, &mis)) != RWN_OK) return st;
+    if ((uintptr_t)rstd % 4) return fail(RWN_ERR_INVALID_ARG, "%s: rstd must be float aligned", fn);
+    Plan p;
+    if ((st = plan_for(fn, LAYER_RMS, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = traced(RWN_K_RMS_FWD, s, [&] {
+        return launch_rms_fwd(p, x_dtype, weight_dtype, x, weight, eps, y, rstd, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
+                               rwn_dtype x_dtype, const float* rstd, const void* weight,
+                               rwn_dtype weight_dtype, float eps, void* dx, void* dweight,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "rmsnorm_bwd";
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, weight_dtype);
+    if (st != RWN_OK) return st;
+    if ((st = check_eps(fn, eps)) != RWN_OK) return st;
+    if (!weight) return fail(RWN_ERR_INVALID_ARG, "%s: weight is required", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ng = partial_cols(LAYER_RMS, N);
+    if (M == 0) return finish_bwd(fn, weight_dtype, nullptr, 0, ng, N, dweight, nullptr, nullptr, s);
+    const void* ops[3] = {x, dy, dx};
+    const char* names[3] = {"x", "dy", "dx"};
+    int mis = 0;
+    if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
+    Plan p;
+    if ((st = plan_for(fn, LAYER_RMS, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = check_workspace(fn, p, LAYER_RMS, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = (float*)workspace;
+    hipError_t e = traced(RWN_K_RMS_BWD, s, [&] {
+        return launch_rms_bwd(p, x_dtype, weight_dtype, x, dy, rstd, weight, eps, dx, ws, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return finish_bwd(fn, weight_dtype, ws, p.grid, ng, N, dweight, nullptr, nullptr, s);
+}
+
+RWN_API rwn_status rmsnorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
+    return workspace_size(LAYER_RMS, M, N, x_dtype, bytes);
+}
+
+// ================================================================================== support
+
+RWN_API const char* rwn_last_error(void) { return g_err; }
+
+RWN_API const char* rwn_version(void) { return "rwnorm 0.1.0 (gfx950)"; }
+
+RWN_API rwn_status rwn_trace_begin(int capacity) {
+    Trace& t = g_trace;
+    if (capacity < 1 || capacity > (1 << 20))
+        return fail(RWN_ERR_INVALID_ARG, "rwn_trace_begin: capacity must be in [1, 2^20]");
+    if (t.on) return fail(RWN_ERR_INVALID_ARG, "rwn_trace_begin: a trace is already running");
+    t.ev.assign((size_t)capacity, TraceEntry{0, nullptr, nullptr});
+    for (int i = 0; i < capacity; ++i) {
+        hipError_t e = hipEventCreate(&t.ev[i].a);
+        if (e == hipSuccess) e = hipEventCreate(&t.ev[i].b);
+        if (e != hipSuccess) {
+            for (int j = 0; j <= i; ++j) {
+                if (t.ev[j].a) (void)hipEventDestroy(t.ev[j].a);
+                if (t.ev[j].b) (void)hipEventDestroy(t.ev[j].b);
+            }
+            t.ev.clear();
+            return hip_fail(e, "rwn_trace_begin: hipEventCreate");
+        }
+    }
+    t.cap = capacity;
+    t.used = 0;
+    t.on = true;
+    return ok();
+}
+
+RWN_API int rwn_trace_end(float* ms, int* tags, int capacity) {
+    Trace& t = g_trace;
+    if (!t.on) {
+        fail(RWN_ERR_INVALID_ARG, "rwn_trace_end: no trace is running");
+        return -1;
+    }
+    int n = 0;
+    int rc = 0;
+    for (int i = 0; i < t.used; ++i) {
+        if (n >= capacity) break;
+        hipError_t e = hipEventSynchronize(t.ev[i].b);
+        float v = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&v, t.ev[i].a, t.ev[i].b);
+        if (e != hipSuccess) {
+            hip_fail(e, "rwn_trace_end");
+            rc = -1;
+            break;
+        }
+        if (ms) ms[n] = v;
+        if (tags) tags[n] = t.ev[i].tag;
+        ++n;
+    }
+    for (auto& e : t.ev) {
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
+    }
+    t.ev.clear();
+    t.on = false;
+    t.cap = t.used = 0;
+    if (rc < 0) return -1;
+    ok();
+    return n;
+}
+
+RWN_API rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
+    if (!src || !dst) return fail(RWN_ERR_INVALID_ARG, "rwn_copy_probe: NULL buffer");
+    if (((uintptr_t)src | (uintptr_t)dst | bytes) % 16)
+        return fail(RWN_ERR_INVALID_ARG, "rwn_copy_probe: buffers and size must be 16-byte multiples");
+    if (bytes == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = traced(RWN_K_COPY, s, [&] { return launch_copy_probe(src, dst, bytes, s); });
+    if (e != hipSuccess) return hip_fail(e, "rwn_copy_probe");
+    return ok();
+}
+
+RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
+                            int misalign_bytes, int cus, int64_t* out) {
+    const char* fn = "rwn_plan";
+    if (!out) return fail(RWN_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (layer < 0 || layer > 2) return fail(RWN_ERR_INVALID_ARG, "%s: layer must be 0, 1 or 2", fn);
+    rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, RWN_F32);
+    if (st != RWN_OK) return st;
+    const int esz = x_dtype == RWN_F32 ? 4 : 2;
+    if (misalign_bytes < 0 || misalign_bytes >= 16 || misalign_bytes % esz)
+        return fail(RWN_ERR_INVALID_ARG, "%s: misalign_bytes must be a multiple of the element size below 16", fn);
+    if (cus < 0) return fail(RWN_ERR_INVALID_ARG, "%s: cus must be >= 0", fn);
+    if (cus == 0 && (st = device_cus(&cus)) != RWN_OK) return st;
+    Plan p;
+    if (!make_plan(layer, backward != 0, M, N, (int)x_dtype, misalign_bytes, cus, &p))
+        return fail(RWN_ERR_UNSUPPORTED, "%s: no launch plan for N = %lld", fn, (long long)N);
+    out[0] = p.mode; out[1] = p.cpt; out[2] = p.rt; out[3] = p.tpr; out[4] = p.rpp;
+    out[5] = p.block; out[6] = p.grid; out[7] = p.ntiles;
+    out[8] = p.mode == MODE_SCALAR ? 1 : 16 / esz;
+    return ok();
+}

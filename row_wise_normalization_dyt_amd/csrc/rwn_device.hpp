@@ -1,0 +1,331 @@
+// Device-side building blocks shared by the DyT, LayerNorm and RMSNorm kernels (gfx950).
+//
+// Thread -> data map used by every row kernel
+// -------------------------------------------
+// A workgroup of `block` threads holds `rpp` row slots of `tpr` threads each (block = rpp*tpr).
+// The thread with local id t owns slot t / tpr and lane t % tpr.  A row is cut into 16-byte
+// chunks (V elements: 4 float32 or 8 bfloat16); lane l owns chunks l, l + tpr, ...,
+// l + (CPT-1)*tpr of every row it visits, so consecutive lanes touch consecutive 16-byte
+// chunks (coalesced) and a thread's columns never change while it walks rows.  That is what
+// lets the backward keep its parameter-gradient partials in registers.
+//
+// Three modes handle every N and base address:
+//   ALIGNED  N % V == 0 and 16-byte-aligned rows: chunk c covers columns [cV, cV+V).
+//   SHIFTED  any N (wide rows only): row r starts s = (b + rN) mod V elements past a 16-byte
+//            boundary; chunk c covers columns [cV - s, cV - s + V).  The launcher makes every
+//            thread visit rows that share one s (grid * rpp divisible by V), so the column map
+//            is still fixed.  Chunks cut by the row ends are loaded/stored element by element.
+//   SCALAR   V = 1 (narrow rows whose chunks would not be 16-byte aligned).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rwn {
+
+typedef __bf16 bf16_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum Mode { MODE_ALIGNED = 0, MODE_SHIFTED = 1, MODE_SCALAR = 2 };
+
+template <typename T> struct ChunkOf;
+template <> struct ChunkOf<float> { static constexpr int value = 4; };
+template <> struct ChunkOf<bf16_t> { static constexpr int value = 8; };
+
+template <typename T, int MODE>
+struct Elems { static constexpr int value = (MODE == MODE_SCALAR) ? 1 : ChunkOf<T>::value; };
+
+// Launch geometry shared by all row kernels (values computed by the host planner).
+struct Geom {
+    int64_t M, N;
+    int64_t ntiles;   // number of row tiles; a tile is rpp * RT rows
+    int tpr;          // threads per row
+    int rpp;          // row slots per workgroup
+    int base_shift;   // SHIFTED: misalignment of the [M, N] base address, in elements
+    float inv_n;      // 1 / N
+};
+
+// ------------------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// gfx950 lowers this to v_cvt_pk_bf16_f32: round to nearest even, NaN preserved.
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)v; }
+
+// The float32 value of v after a round trip through storage dtype T.
+template <typename T> __device__ __forceinline__ float round_through(float v) {
+    return to_f32(from_f32<T>(v));
+}
+
+// ------------------------------------------------------------------------- chunk I/O
+
+template <typename T, int V> struct ChunkIO;
+
+template <> struct ChunkIO<float, 4> {
+    __device__ __forceinline__ static void load(const float* p, float* o) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+    }
+    __device__ __forceinline__ static void store(float* p, const float* o) {
+        f32x4 v = {o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(p) = v;
+    }
+};
+
+template <> struct ChunkIO<bf16_t, 8> {
+    __device__ __forceinline__ static void load(const bf16_t* p, float* o) {
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+        f32x8 f = __builtin_convertvector(v, f32x8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = f[i];
+    }
+    __device__ __forceinline__ static void store(bf16_t* p, const float* o) {
+        f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+        *reinterpret_cast<bf16x8*>(p) = __builtin_convertvector(f, bf16x8);
+    }
+};
+
+template <typename T> struct ChunkIO<T, 1> {
+    __device__ __forceinline__ static void load(const T* p, float* o) { o[0] = to_f32(*p); }
+    __device__ __forceinline__ static void store(T* p, const float* o) { *p = from_f32<T>(o[0]); }
+};
+
+// Per-thread column map: which columns each of the CPT chunks covers (fixed for all rows the
+// thread visits) and whether the chunk is whole inside the row.
+template <typename T, int MODE, int CPT>
+struct ColMap {
+    static constexpr int V = Elems<T, MODE>::value;
+    int col0[CPT];      // column of element 0 of chunk k (may be negative in SHIFTED mode)
+    bool full[CPT];     // all V columns inside [0, N)
+    bool any[CPT];      // at least one column inside [0, N)
+    int shift;          // SHIFTED: s of this thread's rows
+
+    __device__ __forceinline__ void init(int lane, int tpr, int64_t N, int s) {
+        shift = s;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            int c = lane + k * tpr;
+            int j0 = c * V - (MODE == MODE_SHIFTED ? s : 0);
+            col0[k] = j0;
+            full[k] = (j0 >= 0) && ((int64_t)j0 + V <= N);
+            any[k] = ((int64_t)j0 + V > 0) && ((int64_t)j0 < N);
+        }
+    }
+    __device__ __forceinline__ bool valid(int k, int v, int64_t N) const {
+        if (MODE == MODE_SHIFTED) {
+            int j = col0[k] + v;
+            return j >= 0 && (int64_t)j < N;
+        }
+        return any[k];
+    }
+};
+
+// The raw 16-byte chunks of one row slice, kept packed in registers (a bfloat16 pair per
+// 32-bit word) and converted to float32 on use.  SCALAR mode keeps one element per word.
+template <typename T, int MODE, int CPT>
+struct RowRegs {
+    static constexpr int V = Elems<T, MODE>::value;
+    static constexpr int W = (MODE == MODE_SCALAR) ? 1 : 4;   // 32-bit words per chunk
+    uint32_t w[CPT][W];
+
+    __device__ __forceinline__ float get(int k, int v) const {
+        if constexpr (sizeof(T) == 4) {
+            return __builtin_bit_cast(float, w[k][MODE == MODE_SCALAR ? 0 : v]);
+        } else {
+            if (MODE == MODE_SCALAR) return __builtin_bit_cast(float, w[k][0] << 16);
+            const uint32_t u = w[k][v >> 1];
+            return __builtin_bit_cast(float, (v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+        }
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t raw_bits(const T* p) {
+    if constexpr (sizeof(T) == 4) return *reinterpret_cast<const uint32_t*>(p);
+    else return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+}
+
+// Load the CPT chunks of row `row` of p (row pitch N); columns outside the row read as 0, and
+// `rowvalid` false reads nothing (all zeros).
+template <typename T, int MODE, int CPT>
+__device__ __forceinline__ void load_row(const T* __restrict__ p, int64_t row, int64_t N,
+                                         const ColMap<T, MODE, CPT>& cm, bool rowvalid,
+                                         RowRegs<T, MODE, CPT>& r) {
+    constexpr int V = RowRegs<T, MODE, CPT>::V;
+    constexpr int W = RowRegs<T, MODE, CPT>::W;
+    const T* rp = p + row * N;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) r.w[k][i] = 0u;
+        if (!rowvalid || !cm.any[k]) continue;
+        if (MODE == MODE_SCALAR) {
+            r.w[k][0] = raw_bits(rp + cm.col0[k]);
+        } else if (MODE == MODE_ALIGNED || cm.full[k]) {
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = *reinterpret_cast<const u32x4*>(rp + cm.col0[k]);
+            r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int j = cm.col0[k] + v;
+                if (j >= 0 && (int64_t)j < N) {
+                    const uint32_t b = raw_bits(rp + j);
+                    if constexpr (sizeof(T) == 4) r.w[k][v] = b;
+                    else r.w[k][v >> 1] |= b << (16 * (v & 1));
+                }
+            }
+        }
+    }
+}
+
+// Store chunk k of row `row` from V float32 values (rounded to T); only columns inside the row.
+template <typename T, int MODE, int CPT>
+__device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int64_t N,
+                                            const ColMap<T, MODE, CPT>& cm, int k, const float* o) {
+    constexpr int V = ColMap<T, MODE, CPT>::V;
+    if (!cm.any[k]) return;
+    T* rp = p + row * N;
+    if (MODE != MODE_SHIFTED || cm.full[k]) {
+        ChunkIO<T, V>::store(rp + cm.col0[k], o);
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const int j = cm.col0[k] + v;
+            if (j >= 0 && (int64_t)j < N) rp[j] = from_f32<T>(o[v]);
+        }
+    }
+}
+
+// Load a per-column parameter vector for this thread's columns (0 outside [0, N)).
+template <typename T, typename PT, int MODE, int CPT>
+__device__ __forceinline__ void load_param(const PT* __restrict__ p, int64_t N,
+                                           const ColMap<T, MODE, CPT>& cm, float* o) {
+    constexpr int V = ColMap<T, MODE, CPT>::V;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            int j = cm.col0[k] + v;
+            o[k * V + v] = (j >= 0 && (int64_t)j < N && cm.any[k]) ? to_f32(p[j]) : 0.f;
+        }
+}
+
+// ------------------------------------------------------------------- row reductions
+// All reductions must be called by every lane of the wave (uniform control flow): DPP and
+// swizzle read neighbouring lanes.  Each step adds a value and its partner's; since float
+// addition is commutative both lanes of a pair get the same bits, so every lane of a group
+// ends with the identical sum.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    // ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 (within 32-lane halves).
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of `g` lanes (g a power of two, 1..64); result in every lane.
+__device__ __forceinline__ float group_sum(float v, int g) {
+    if (g >= 2) v += dpp_f<DPP_QUAD_XOR1>(v);
+    if (g >= 4) v += dpp_f<DPP_QUAD_XOR2>(v);
+    if (g >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+    if (g >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
+    if (g >= 32) v += swizzle_xor16(v);
+    if (g >= 64) v = readlane_f(v, 0) + readlane_f(v, 32);
+    return v;
+}
+
+// Row sums for K values per thread.  Rows of up to 64 threads reduce inside their wave; rows
+// spanning W = tpr/64 waves add the W wave sums from LDS in wave order.  `red` holds
+// 2 * (block/64) * K floats; `parity` alternates between two halves so one barrier per
+// reduction is enough.
+template <int K>
+__device__ __forceinline__ void row_sum(float (&v)[K], int tpr, float* red, int& parity) {
+    const int g = tpr < 64 ? tpr : 64;
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = group_sum(v[i], g);
+    if (tpr > 64) {
+        const int nw = blockDim.x >> 6;
+        const int wave = threadIdx.x >> 6;
+        float* buf = red + parity * nw * K;
+        if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+            for (int i = 0; i < K; ++i) buf[wave * K + i] = v[i];
+        }
+        __syncthreads();
+        const int w_per_row = tpr >> 6;
+        const int first = (wave / w_per_row) * w_per_row;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            float s = buf[first * K + i];
+            for (int w = 1; w < w_per_row; ++w) s += buf[(first + w) * K + i];
+            v[i] = s;
+        }
+        parity ^= 1;
+    }
+}
+
+// Sum of one value over the whole workgroup, in wave order; valid in thread 0.
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+    v = group_sum(v, 64);
+    const int nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float s = 0.f;
+    if (threadIdx.x == 0) {
+        s = scratch[0];
+        for (int w = 1; w < nw; ++w) s += scratch[w];
+    }
+    return s;
+}
+
+// ------------------------------------------------------------------- tanh and sech^2
+// From e = exp(-2|z|): tanh|z| = (1 - e) / (1 + e) and sech^2 z = 4e / (1 + e)^2, both
+// without cancellation except 1 - e near z = 0; there tanh uses its Taylor series
+// z - z^3/3 + 2z^5/15 - 17z^7/315 (|z| < 1/8: truncation error below 2e-10 relative).
+// z = +-inf gives e = 0: tanh = +-1, sech^2 = 0 exactly.
+struct TanhSech2 { float t, s; };
+
+__device__ __forceinline__ TanhSech2 tanh_sech2(float z) {
+    const float az = __builtin_fabsf(z);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * az);   // 2 * log2(e)
+    const float q = __builtin_amdgcn_rcpf(1.0f + e);
+    const float tb = (1.0f - e) * q;
+    const float z2 = z * z;
+    const float ts = z * __builtin_fmaf(z2, __builtin_fmaf(z2, __builtin_fmaf(z2, -0.05396825396825397f,
+                                         0.13333333333333333f), -0.33333333333333333f), 1.0f) ;
+    TanhSech2 r;
+    r.t = az < 0.125f ? ts : __builtin_copysignf(tb, z);
+    r.s = 4.0f * e * q * q;
+    return r;
+}
+
+__device__ __forceinline__ float tanh_only(float z) {
+    const float az = __builtin_fabsf(z);
+    const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * az);
+    const float tb = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+    const float z2 = z * z;
+    const float ts = z * __builtin_fmaf(z2, __builtin_fmaf(z2, __builtin_fmaf(z2, -0.05396825396825397f,
+                                         0.13333333333333333f), -0.33333333333333333f), 1.0f);
+    return az < 0.125f ? ts : __builtin_copysignf(tb, z);
+}
+
+}  // namespace rwn

@@ -1,0 +1,537 @@
+// Row kernels for DyT, LayerNorm and RMSNorm, forward and backward stage 1, plus the
+// stage-2 column reduction (gfx950, wave64).
+//
+// Every row kernel runs a persistent 1D grid: workgroup w visits row tiles w, w + grid, ...
+// (a tile is rpp * RT rows), so M is bounded only by 64-bit indexing, and the number of
+// workgroups -- which is also the number of partial rows of the backward -- is chosen by the
+// host from the device's CU count.  Each thread reads its x (and dy) chunks of a row once
+// into registers, reduces across the row's threads (DPP inside a wave, LDS across waves),
+// and writes y or dx from the same registers.
+//
+// Backward stage 1 accumulates the parameter-gradient terms of its columns in float32
+// registers over every row the thread visits, then writes one partial row per workgroup to
+// the workspace [grid, ng] (ng = 2N+1 DyT: dgamma | dbeta | dalpha; 2N LayerNorm:
+// dgamma | dbeta; N RMSNorm: dweight).  Row slots of a workgroup are combined in slot order
+// through LDS.  Stage 2 sums the partial rows per column in a fixed order in float64.  No
+// atomics anywhere: the reduction order depends only on the launch plan.
+#pragma once
+
+#include "rwn_device.hpp"
+
+namespace rwn {
+
+constexpr int kMaxBlock = 1024;
+// Narrow plans (RT > 1) always run 256-thread workgroups; wide plans up to 1024.
+template <int RT> struct MaxBlock { static constexpr int value = RT > 1 ? 256 : kMaxBlock; };
+constexpr int kRedFloats = 2 * (kMaxBlock / 64) * 8;   // row_sum buffers: 2 halves x waves x K<=8
+
+// Per-thread setup common to all row kernels.
+template <typename T, int MODE, int CPT, int RT>
+struct RowCtx {
+    int slot, lane;
+    int64_t rows_per_tile;
+    ColMap<T, MODE, CPT> cm;
+
+    __device__ __forceinline__ RowCtx(const Geom& g) {
+        slot = threadIdx.x / g.tpr;
+        lane = threadIdx.x - slot * g.tpr;
+        rows_per_tile = (int64_t)g.rpp * RT;
+        int s = 0;
+        if (MODE == MODE_SHIFTED) {
+            // All rows this thread visits differ by a multiple of V (host guarantee), so the
+            // first one fixes the shift.
+            const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile + slot;
+            s = (int)(((int64_t)g.base_shift + r0 * g.N) % ColMap<T, MODE, CPT>::V);
+        }
+        cm.init(lane, g.tpr, g.N, s);
+    }
+    __device__ __forceinline__ int64_t row(int64_t tile, int u, const Geom& g) const {
+        return tile * rows_per_tile + (int64_t)u * g.rpp + slot;
+    }
+};
+
+// Load a per-column parameter (or `dflt` for every column when p is NULL).
+template <typename T, typename PT, int MODE, int CPT>
+__device__ __forceinline__ void load_param_or(const PT* __restrict__ p, float dflt, int64_t N,
+                                              const ColMap<T, MODE, CPT>& cm, float* o) {
+    constexpr int E = CPT * ColMap<T, MODE, CPT>::V;
+    if (p) {
+        load_param<T, PT, MODE, CPT>(p, N, cm, o);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = dflt;
+    }
+}
+
+// Write one gradient's partial row: out[col] = sum over row slots (slot order) of acc.
+// `part` is E * blockDim.x floats of LDS (only used when rpp > 1).
+template <typename T, int MODE, int CPT>
+__device__ __forceinline__ void write_partial(float* __restrict__ out, const float* acc,
+                                              const ColMap<T, MODE, CPT>& cm, int slot, int lane,
+                                              const Geom& g, float* part) {
+    constexpr int V = ColMap<T, MODE, CPT>::V;
+    constexpr int E = CPT * V;
+    if (g.rpp == 1) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (cm.valid(k, v, g.N)) out[cm.col0[k] + v] = acc[k * V + v];
+        return;
+    }
+    const int nb = blockDim.x;
+    __syncthreads();   // previous users of `part` are done
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[e * nb + threadIdx.x] = acc[e];
+    __syncthreads();
+    if (slot == 0) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int e = k * V + v;
+                float s = part[e * nb + lane];
+                for (int sl = 1; sl < g.rpp; ++sl) s += part[e * nb + sl * g.tpr + lane];
+                if (cm.valid(k, v, g.N)) out[cm.col0[k] + v] = s;
+            }
+    }
+}
+
+// ================================================================================== DyT
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
+               const PT* __restrict__ gamma, const PT* __restrict__ beta, T* __restrict__ y,
+               Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float ga[E], be[E];
+    load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
+    load_param<T, PT, MODE, CPT>(beta, g.N, c.cm, be);
+    const float alpha = to_f32(alpha_p[0]);
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            if (!ok[u]) continue;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * xr[u].get(k, v)), be[k * V + v]);
+                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+            }
+        }
+    }
+}
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
+               const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws,
+               int64_t ng, Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    extern __shared__ float part[];
+    __shared__ float red[kRedFloats];
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float ga[E];
+    load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
+    const float alpha = to_f32(alpha_p[0]);
+    float acc_g[E], acc_b[E], acc_a = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
+
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT], gr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int e = k * V + v;
+                    const float xv = xr[u].get(k, v), gv = gr[u].get(k, v);
+                    const TanhSech2 ts = tanh_sech2(alpha * xv);
+                    // alpha * sech^2 is 0 wherever sech^2 is 0 (alpha = +inf would give inf * 0).
+                    const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
+                    const float d = gv * ga[e];
+                    // Contributions of padded rows and columns are dropped after the arithmetic:
+                    // a padded x = 0 with alpha = +inf makes NaN, which must not reach a sum.
+                    const bool live = ok[u] && c.cm.valid(k, v, g.N);
+                    acc_g[e] += live ? gv * ts.t : 0.f;
+                    acc_b[e] += live ? gv : 0.f;
+                    acc_a += live ? d * xv * ts.s : 0.f;
+                    o[v] = d * as;
+                }
+                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+            }
+        }
+    }
+    float* out = ws + (int64_t)blockIdx.x * ng;
+    write_partial<T, MODE, CPT>(out, acc_g, c.cm, c.slot, c.lane, g, part);
+    write_partial<T, MODE, CPT>(out + g.N, acc_b, c.cm, c.slot, c.lane, g, part);
+    const float da = block_sum(acc_a, red);
+    if (threadIdx.x == 0) out[2 * g.N] = da;
+}
+
+// ============================================================================ LayerNorm
+
+// mean and rstd of RT rows (two passes over the registers: sum, then sum of squared
+// deviations).
+template <typename T, int MODE, int CPT, int RT>
+__device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
+                                         const ColMap<T, MODE, CPT>& cm, const Geom& g, float eps,
+                                         float* red, int& parity, float (&mu)[RT], float (&rs)[RT]) {
+    constexpr int V = Elems<T, MODE>::value;
+    float s[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) a += xr[u].get(k, v);
+        s[u] = a;
+    }
+    row_sum<RT>(s, g.tpr, red, parity);
+#pragma unroll
+    for (int u = 0; u < RT; ++u) mu[u] = s[u] * g.inv_n;
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float d = xr[u].get(k, v) - mu[u];
+                a += cm.valid(k, v, g.N) ? d * d : 0.f;
+            }
+        s[u] = a;
+    }
+    row_sum<RT>(s, g.tpr, red, parity);
+#pragma unroll
+    for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
+}
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta,
+              float eps, T* __restrict__ y, float* __restrict__ mean_out,
+              float* __restrict__ rstd_out, Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    __shared__ float red[kRedFloats];
+    int parity = 0;
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float ga[E], be[E];
+    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
+    load_param_or<T, PT, MODE, CPT>(beta, 0.f, g.N, c.cm, be);
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+        }
+        float mu[RT], rs[RT];
+        ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            if (!ok[u]) continue;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    o[v] = __builtin_fmaf((xr[u].get(k, v) - mu[u]) * rs[u], ga[k * V + v], be[k * V + v]);
+                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+            }
+            if (c.lane == 0) {
+                if (mean_out) mean_out[row[u]] = mu[u];
+                if (rstd_out) rstd_out[row[u]] = rs[u];
+            }
+        }
+    }
+}
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
+              const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
+              T* __restrict__ dx, float* __restrict__ ws, int64_t ng, Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    extern __shared__ float part[];
+    __shared__ float red[kRedFloats];
+    int parity = 0;
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float ga[E];
+    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
+    const bool have_stats = mean_in != nullptr && rstd_in != nullptr;
+    float acc_g[E], acc_b[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
+
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT], gr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+        float mu[RT], rs[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+            if (have_stats) {
+                mu[u] = ok[u] ? mean_in[row[u]] : 0.f;
+                rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
+            }
+        }
+        if (!have_stats) ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
+        float s[2 * RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
+                    const float gg = gr[u].get(k, v) * ga[k * V + v];
+                    const bool cv = c.cm.valid(k, v, g.N);
+                    a += cv ? gg : 0.f;
+                    b += cv ? gg * xh : 0.f;
+                }
+            s[2 * u] = a;
+            s[2 * u + 1] = b;
+        }
+        row_sum<2 * RT>(s, g.tpr, red, parity);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            const float c1 = s[2 * u] * g.inv_n, c2 = s[2 * u + 1] * g.inv_n;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int e = k * V + v;
+                    const float gv = gr[u].get(k, v);
+                    const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
+                    const bool live = ok[u] && c.cm.valid(k, v, g.N);
+                    acc_g[e] += live ? gv * xh : 0.f;
+                    acc_b[e] += live ? gv : 0.f;
+                    o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
+                }
+                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+            }
+        }
+    }
+    float* out = ws + (int64_t)blockIdx.x * ng;
+    write_partial<T, MODE, CPT>(out, acc_g, c.cm, c.slot, c.lane, g, part);
+    write_partial<T, MODE, CPT>(out + g.N, acc_b, c.cm, c.slot, c.lane, g, part);
+}
+
+// ============================================================================== RMSNorm
+
+template <typename T, int MODE, int CPT, int RT>
+__device__ __forceinline__ void rms_stats(const RowRegs<T, MODE, CPT> (&xr)[RT], const Geom& g,
+                                          float eps, float* red, int& parity, float (&rs)[RT]) {
+    constexpr int V = Elems<T, MODE>::value;
+    float s[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float xv = xr[u].get(k, v);
+                a = __builtin_fmaf(xv, xv, a);
+            }
+        s[u] = a;
+    }
+    row_sum<RT>(s, g.tpr, red, parity);
+#pragma unroll
+    for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
+}
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps,
+               T* __restrict__ y, float* __restrict__ rstd_out, Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    __shared__ float red[kRedFloats];
+    int parity = 0;
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float w[E];
+    load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+        }
+        float rs[RT];
+        rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            if (!ok[u]) continue;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+                // One rounding of the normalized value to x's dtype, then the weight multiply
+                // in float32; the store rounds the product to x's dtype.
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    o[v] = w[k * V + v] * round_through<T>(xr[u].get(k, v) * rs[u]);
+                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+            }
+            if (c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
+        }
+    }
+}
+
+template <typename T, typename PT, int MODE, int CPT, int RT>
+__global__ void __launch_bounds__(MaxBlock<RT>::value)
+rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
+               const PT* __restrict__ weight, float eps, T* __restrict__ dx,
+               float* __restrict__ ws, int64_t ng, Geom g) {
+    constexpr int V = Elems<T, MODE>::value;
+    constexpr int E = CPT * V;
+    extern __shared__ float part[];
+    __shared__ float red[kRedFloats];
+    int parity = 0;
+    RowCtx<T, MODE, CPT, RT> c(g);
+    float w[E];
+    load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    float acc_w[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc_w[e] = 0.f;
+
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        RowRegs<T, MODE, CPT> xr[RT], gr[RT];
+        bool ok[RT];
+        int64_t row[RT];
+        float rs[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            row[u] = c.row(tile, u, g);
+            ok[u] = row[u] < g.M;
+            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+            if (rstd_in) rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
+        }
+        if (!rstd_in) rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
+        float s[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    // grad of the normalized value: the float32 product rounded to x's dtype.
+                    const float gg = round_through<T>(gr[u].get(k, v) * w[k * V + v]);
+                    a = __builtin_fmaf(gg, xr[u].get(k, v) * rs[u], a);
+                }
+            s[u] = a;
+        }
+        row_sum<RT>(s, g.tpr, red, parity);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            const float cc = s[u] * g.inv_n;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float o[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int e = k * V + v;
+                    const float gv = gr[u].get(k, v);
+                    const float h = xr[u].get(k, v) * rs[u];
+                    const float gg = round_through<T>(gv * w[e]);
+                    // weight-gradient term: dy * n rounded to the weight's dtype before the sum.
+                    const float term = round_through<PT>(gv * round_through<T>(h));
+                    acc_w[e] += (ok[u] && c.cm.valid(k, v, g.N)) ? term : 0.f;
+                    o[v] = rs[u] * (gg - h * cc);
+                }
+                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+            }
+        }
+    }
+    float* out = ws + (int64_t)blockIdx.x * ng;
+    write_partial<T, MODE, CPT>(out, acc_w, c.cm, c.slot, c.lane, g, part);
+}
+
+// ============================================================================ stage 2
+
+// out columns: [0, N) -> out0, [N, 2N) -> out1, 2N -> out2[0] (NULL outputs are skipped).
+// Workgroup of `blockDim.x` threads = cb columns x G partial-row lanes; lane l adds partial
+// rows l, l + G, ... in order in float64, then the G lane sums are added as a fixed tree.
+template <typename PT>
+__global__ void __launch_bounds__(512)
+colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t N, int cb,
+                 PT* __restrict__ out0, PT* __restrict__ out1, PT* __restrict__ out2) {
+    __shared__ double red[512];
+    const int G = blockDim.x / cb;
+    const int cl = threadIdx.x % cb, gl = threadIdx.x / cb;
+    const int64_t col = (int64_t)blockIdx.x * cb + cl;
+    double acc = 0.0;
+    if (col < ng) {
+        int64_t p = gl;
+        for (; p + 3 * G < P; p += 4 * G) {
+            const float a0 = ws[p * ng + col], a1 = ws[(p + G) * ng + col];
+            const float a2 = ws[(p + 2 * G) * ng + col], a3 = ws[(p + 3 * G) * ng + col];
+            acc += a0; acc += a1; acc += a2; acc += a3;
+        }
+        for (; p < P; p += G) acc += ws[p * ng + col];
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int st = G / 2; st > 0; st >>= 1) {
+        if (gl < st) red[gl * cb + cl] += red[(gl + st) * cb + cl];
+        __syncthreads();
+    }
+    if (gl == 0 && col < ng) {
+        const PT v = from_f32<PT>((float)red[cl]);
+        if (col < N) {
+            if (out0) out0[col] = v;
+        } else if (col < 2 * N) {
+            if (out1) out1[col - N] = v;
+        } else {
+            if (out2) out2[0] = v;
+        }
+    }
+}
+
+}  // namespace rwn

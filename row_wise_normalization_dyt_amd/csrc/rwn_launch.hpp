@@ -1,0 +1,113 @@
+// Host-side launch plan and kernel dispatch (shared by the launcher and API translation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rwn_device.hpp"
+
+namespace rwn {
+
+enum Layer { LAYER_DYT = 0, LAYER_LN = 1, LAYER_RMS = 2 };
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// Widest row a plan covers: 16 waves x 64 lanes x CPT chunks (CPT <= 2 for bf16, 4 for f32).
+constexpr int64_t kMaxN = 16384;
+
+struct Plan {
+    int mode = MODE_ALIGNED;  // Mode
+    int cpt = 1;              // 16-byte chunks per thread per row
+    int rt = 1;               // rows per thread per tile
+    int tpr = 1;              // threads per row
+    int rpp = 1;              // row slots per workgroup
+    int block = 64;           // workgroup size
+    int64_t ntiles = 0;       // row tiles of rpp * rt rows
+    int64_t grid = 0;         // workgroups (= partial rows of a backward)
+    int base_shift = 0;       // SHIFTED: base misalignment in elements
+    size_t lds_bytes = 0;     // dynamic LDS of the backward stage 1
+    int64_t M = 0, N = 0;
+};
+
+// Plan for one call.  misalign_bytes: address of the [M, N] operands modulo 16 (a multiple of
+// the element size).  cus: compute units of the device.  Returns false if N is too wide.
+bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misalign_bytes,
+               int cus, Plan* out);
+
+// Partial-row columns of a backward: 2N+1 (DyT), 2N (LayerNorm), N (RMSNorm).
+inline int64_t partial_cols(int layer, int64_t N) {
+    return layer == LAYER_DYT ? 2 * N + 1 : layer == LAYER_LN ? 2 * N : N;
+}
+
+inline Geom make_geom(const Plan& p) {
+    Geom g;
+    g.M = p.M;
+    g.N = p.N;
+    g.ntiles = p.ntiles;
+    g.tpr = p.tpr;
+    g.rpp = p.rpp;
+    g.base_shift = p.base_shift;
+    g.inv_n = 1.0f / (float)p.N;
+    return g;
+}
+
+template <int V> using IC = std::integral_constant<int, V>;
+template <typename T> struct TypeTag { using type = T; };
+
+// Calls f(TypeTag<T>, TypeTag<PT>) for the supported dtype pairs.
+template <typename F>
+hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
+    if (xdt == DT_F32 && pdt == DT_F32) return f(TypeTag<float>{}, TypeTag<float>{});
+    if (xdt == DT_BF16 && pdt == DT_F32) return f(TypeTag<bf16_t>{}, TypeTag<float>{});
+    if (xdt == DT_BF16 && pdt == DT_BF16) return f(TypeTag<bf16_t>{}, TypeTag<bf16_t>{});
+    return hipErrorInvalidValue;
+}
+
+// Calls f(IC<MODE>, IC<CPT>, IC<RT>) for the instantiated shapes.  Vector modes use CPT = 4
+// only for float32 (E = CPT * V <= 16 elements per thread per row).
+template <typename T, typename F>
+hipError_t dispatch_shape(const Plan& p, F&& f) {
+    constexpr bool f32 = sizeof(T) == 4;
+    if (p.mode == MODE_ALIGNED) {
+        if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{});
+        if (p.rt == 1) {
+            if (p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{});
+            if (p.cpt == 2) return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{});
+            if constexpr (f32) if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{});
+        }
+    } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
+        if (p.cpt == 1) return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{});
+        if (p.cpt == 2) return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{});
+        if constexpr (f32) if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{});
+    } else if (p.mode == MODE_SCALAR && p.rt == 1) {
+        if (p.cpt == 1) return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{});
+        if (p.cpt == 2) return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{});
+        if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{});
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- launchers (one per kernel)
+hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                          const void* gamma, const void* beta, void* y, hipStream_t s);
+hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                          const void* alpha, const void* gamma, void* dx, float* ws,
+                          hipStream_t s);
+hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
+                         const void* beta, float eps, void* y, float* mean, float* rstd,
+                         hipStream_t s);
+hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                         const float* mean, const float* rstd, const void* gamma, float eps,
+                         void* dx, float* ws, hipStream_t s);
+hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* w,
+                          float eps, void* y, float* rstd, hipStream_t s);
+hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                          const float* rstd, const void* w, float eps, void* dx, float* ws,
+                          hipStream_t s);
+// Stage 2: P partial rows of ng columns -> out0 [N], out1 [N], out2 [1] in param dtype pdt.
+hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t N,
+                            void* out0, void* out1, void* out2, hipStream_t s);
+hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace rwn

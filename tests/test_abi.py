@@ -1,0 +1,156 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/rwnorm.h declares,
+rejects invalid arguments before touching a device, and plans launches that cover every row
+and column.  No kernel runs here."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+from row_wise_normalization_dyt_amd import _lib
+import row_wise_normalization_dyt_amd as rwn
+
+I64 = ctypes.c_int64
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = _lib.declared_functions()
+    assert {"dyt_fwd", "dyt_bwd", "layernorm_fwd", "layernorm_bwd", "rmsnorm_fwd", "rmsnorm_bwd"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_library_is_built_for_gfx950():
+    with open(_lib.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob
+
+
+def test_version(lib):
+    assert b"rwnorm" in lib.rwn_version()
+
+
+def _err(lib):
+    return lib.rwn_last_error().decode()
+
+
+P = ctypes.c_void_p(16)   # a non-NULL, 16-byte-aligned stand-in pointer; never dereferenced
+
+
+@pytest.mark.parametrize("M,N,code", [(-1, 8, 1), (4, 0, 1), (4, -3, 1), (4, 16385, 2)])
+def test_shape_errors(lib, M, N, code):
+    assert lib.dyt_fwd(M, N, P, 0, P, P, P, 0, P, None) == code
+    assert _err(lib).startswith("dyt_fwd")
+    assert lib.layernorm_fwd(M, N, P, 0, P, P, 0, 1e-5, P, None, None, None) == code
+    assert lib.rmsnorm_bwd(M, N, P, P, 0, None, P, 0, 1e-6, P, P, P, 1 << 20, None) == code
+
+
+def test_dtype_errors(lib):
+    assert lib.dyt_fwd(4, 8, P, 7, P, P, P, 0, P, None) == 1
+    assert lib.dyt_fwd(4, 8, P, 0, P, P, P, 9, P, None) == 1
+    assert lib.rmsnorm_fwd(4, 8, P, 0, P, 1, 1e-6, P, None, None) == 2     # f32 x, bf16 weight
+    assert "not supported" in _err(lib)
+
+
+def test_null_and_eps_errors(lib):
+    assert lib.dyt_fwd(4, 8, P, 0, None, P, P, 0, P, None) == 1
+    assert lib.dyt_bwd(4, 8, P, P, 0, P, None, 0, P, None, None, None, P, 1 << 20, None) == 1
+    assert lib.rmsnorm_fwd(4, 8, P, 1, None, 1, 1e-6, P, None, None) == 1
+    for eps in (-1e-5, float("inf"), float("nan")):
+        assert lib.layernorm_fwd(4, 8, P, 0, P, P, 0, eps, P, None, None, None) == 1
+        assert "eps" in _err(lib)
+    # mean without rstd
+    assert lib.layernorm_bwd(4, 8, P, P, 0, P, None, P, 0, 1e-5, P, None, None, P, 1 << 20, None) == 1
+
+
+def test_operand_alignment_errors(lib):
+    odd = ctypes.c_void_p(16 + 2)
+    # float32 operands must be 4-byte aligned
+    assert lib.dyt_fwd(4, 8, odd, 0, P, P, P, 0, P, None) == 1
+    # bf16 operands with different addresses modulo 16
+    assert lib.dyt_fwd(4, 8, odd, 1, P, P, P, 0, P, None) == 2
+    assert "modulo 16" in _err(lib)
+
+
+def test_empty_forward_is_a_no_op_without_device(lib):
+    assert lib.dyt_fwd(0, 8, None, 1, P, P, P, 0, None, None) == 0
+    assert lib.layernorm_fwd(0, 8, None, 1, None, None, 0, 1e-5, None, None, None, None) == 0
+    assert lib.rmsnorm_fwd(0, 8, None, 1, P, 1, 1e-6, None, None, None) == 0
+    # a backward with no gradient requested has nothing to write
+    assert lib.rmsnorm_bwd(0, 8, None, None, 1, None, P, 1, 1e-6, None, None, None, 0, None) == 0
+    assert _err(lib) == ""
+
+
+def test_workspace_query_errors(lib):
+    out = ctypes.c_size_t(123)
+    assert lib.dyt_bwd_workspace_size(0, 8, 0, ctypes.byref(out)) == 0 and out.value == 0
+    assert lib.layernorm_bwd_workspace_size(-1, 8, 0, ctypes.byref(out)) == 1
+    assert lib.rmsnorm_bwd_workspace_size(5, 8, 0, None) == 1
+
+
+def test_trace_and_probe_argument_errors(lib):
+    assert lib.rwn_trace_begin(0) == 1
+    assert lib.rwn_trace_end(None, None, 0) == -1
+    assert lib.rwn_copy_probe(None, P, 16, None) == 1
+    assert lib.rwn_copy_probe(P, P, 24, None) == 1
+
+
+# ------------------------------------------------------------------------------ planning
+
+SHAPES = [(1, 1), (7, 24), (4096, 64), (401408, 24), (1048573, 32), (1048573, 128), (1048573, 256),
+          (16384, 2048), (8192, 4096), (65536, 1025), (65536, 4096), (65536, 8192), (65536, 16384),
+          (3, 7), (257, 17), (7, 129), (4099, 130), (7, 2049), (65537, 255), (5, 1023)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("backward", [False, True])
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_plan_covers_rows_and_columns(M, N, dtype, backward):
+    esz = 4 if dtype == torch.float32 else 2
+    for mis in range(0, 16, esz):
+        for layer in ("dyt", "layernorm", "rmsnorm"):
+            V = 16 // esz
+            if (N % V or mis) and N > 16384 - (V - 1):
+                # documented limit: a misaligned row of this width needs a 2049th chunk slot
+                with pytest.raises(rwn.RwnError, match="UNSUPPORTED"):
+                    rwn.plan(layer, backward, M, N, dtype, misalign_bytes=mis, cus=256)
+                continue
+            p = rwn.plan(layer, backward, M, N, dtype, misalign_bytes=mis, cus=256)
+            V = p["vec"]
+            # chunks of a row: worst shift is V-1 elements in the shifted mode
+            chunks = -(-(N + (V - 1 if p["mode"] == 1 else 0)) // V)
+            assert p["tpr"] * p["cpt"] >= chunks, p
+            assert p["block"] == p["tpr"] * p["rpp"] and p["block"] <= 1024 and p["block"] % 64 == 0 or p["block"] < 64
+            assert p["tpr"] <= 64 and (p["tpr"] & (p["tpr"] - 1)) == 0 or p["tpr"] % 64 == 0, p
+            if p["mode"] == 0:
+                assert N % V == 0 and mis == 0
+            if p["mode"] == 1:
+                assert p["rpp"] == 1 and p["rt"] == 1
+            rows_per_tile = p["rpp"] * p["rt"]
+            assert p["ntiles"] * rows_per_tile >= M > (p["ntiles"] - 1) * rows_per_tile
+            assert 1 <= p["grid"] <= max(p["ntiles"], 1)
+            if p["grid"] < p["ntiles"]:
+                # every thread of a shifted plan must revisit rows with the same shift
+                assert (p["grid"] * p["rpp"]) % V == 0
+
+
+def test_plan_uses_narrow_tiles_for_narrow_rows():
+    p = rwn.plan("layernorm", True, 401408, 24, torch.float32, cus=256)
+    assert p["mode"] == 0 and p["tpr"] == 8 and p["rpp"] == 32 and p["rt"] == 4
+    p = rwn.plan("dyt", True, 1048573, 32, torch.bfloat16, cus=256)
+    assert p["tpr"] == 4 and p["rpp"] == 64
+    # short input: the tile count caps the grid (no full grid for one row)
+    p = rwn.plan("rmsnorm", False, 1, 128, torch.bfloat16, cus=256)
+    assert p["grid"] == 1 and p["ntiles"] == 1
+
+
+def test_plan_is_deterministic():
+    a = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
+    b = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
+    assert a == b

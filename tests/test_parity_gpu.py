@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element (needs an MI355X).
+
+Bars (tests/tolerance.py): float32 y/dx within 1e-5 of the magnitude sum of their terms;
+bfloat16 y/dx within one bf16 ulp plus that; parameter gradients within 1e-4 of the column's
+sum of |terms| plus one ulp of the parameter dtype; NaN/Inf only where the oracle has them.
+Parameter gradients must also be bitwise identical from run to run.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import row_wise_normalization_dyt_amd as rwn
+import workloads
+from tests import gpu_cases as gc
+from tests import tolerance as tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+LAYERS = ("dyt", "layernorm", "rmsnorm")
+DTYPE_PAIRS = (("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"))
+
+
+def _banner(*a):
+    print("case:", *a, flush=True)
+
+
+def _run_small(layer, M, N, xdt, pdt, seed=3, use_stats=True, **kw):
+    wl = workloads.small(layer, M, N, xdt, pdt, seed=seed, **kw)
+    _banner(wl)
+    return gc.check_workload(wl, DEV, use_stats=use_stats)
+
+
+# ------------------------------------------------------------------ small shapes, all layers
+
+@pytest.mark.parametrize("xdt,pdt", DTYPE_PAIRS)
+@pytest.mark.parametrize("layer", LAYERS)
+def test_small_shapes_span_tiles_and_ragged_tails(layer, xdt, pdt):
+    reps = []
+    for (M, N) in [(4099, 24), (1031, 64), (777, 128), (515, 256), (263, 1024), (130, 2048), (67, 4096)]:
+        reps += _run_small(layer, M, N, xdt, pdt)
+    tol.assert_reports(reps)
+
+
+EDGE_N = [1, 2, 3, 7, 15, 16, 17, 24, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257,
+          1023, 1024, 1025, 2048, 2049]
+
+
+@pytest.mark.parametrize("xdt,pdt", DTYPE_PAIRS)
+@pytest.mark.parametrize("layer", LAYERS)
+def test_edge_widths(layer, xdt, pdt):
+    """Widths around every chunk, wave and mode boundary, at row counts of 1, 7 and 257."""
+    reps = []
+    for N in EDGE_N:
+        for M in (1, 7, 257):
+            reps += _run_small(layer, M, N, xdt, pdt, seed=N * 7 + M)
+    tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_edge_row_counts(layer):
+    reps = []
+    for M in (2, 3, 65535, 65536, 65537):
+        for N in (24, 129):
+            reps += _run_small(layer, M, N, "bf16", "f32", seed=M % 1000)
+    tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_backward_without_saved_stats(layer):
+    if layer == "dyt":
+        pytest.skip("DyT has no statistics")
+    reps = []
+    for (M, N) in [(1001, 24), (257, 1025), (33, 4096)]:
+        reps += _run_small(layer, M, N, "bf16", "f32", use_stats=False)
+    tol.assert_reports(reps)
+
+
+def test_layernorm_without_affine():
+    wl = workloads.small("layernorm", 999, 48, "f32", "f32", seed=5)
+    inp = workloads.make_inputs(wl)
+    del inp["gamma"], inp["beta"]
+    _banner(wl, "no affine")
+    tol.assert_reports(gc.check_workload(wl, DEV, inputs=inp))
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+@pytest.mark.parametrize("offset", [1, 3])
+def test_misaligned_operands_take_the_shifted_path(layer, offset):
+    """x and dy are views starting `offset` bf16 elements past a 16-byte boundary."""
+    reps = []
+    for (M, N) in [(513, 1025), (100, 999), (37, 129), (65, 24)]:
+        wl = workloads.small(layer, M, N, "bf16", "f32", seed=M + offset)
+        _banner(wl, "offset", offset)
+        inp = workloads.make_inputs(wl)
+        dev = {}
+        for k, v in inp.items():
+            if k in ("x", "dy"):
+                buf = torch.empty(v.numel() + 16, dtype=v.dtype, device=DEV)
+                view = buf[offset:offset + v.numel()].view(v.shape)
+                view.copy_(v.to(DEV))
+                assert view.data_ptr() % 16 == 2 * offset
+                dev[k] = view
+            else:
+                dev[k] = v.to(DEV)
+        g = gc.gpu_run(layer, dev, wl.eps)
+        o = gc.oracle_run(layer, inp, wl.eps)
+        reps += gc.compare(layer, g, o, torch.bfloat16, torch.float32)
+    tol.assert_reports(reps)
+
+
+def test_non_contiguous_and_batched_inputs():
+    """Any leading shape; a transposed (non-contiguous) input is copied by the binding."""
+    wl = workloads.small("rmsnorm", 2 * 300 * 32, 128, "bf16", "bf16", seed=11)
+    inp = workloads.make_inputs(wl)
+    x4 = inp["x"].reshape(2, 300, 32, 128).to(DEV)
+    y4, _ = rwn.rmsnorm_fwd(x4, inp["weight"].to(DEV), wl.eps)
+    assert y4.shape == x4.shape
+    xt = inp["x"].reshape(600, 32, 128).transpose(0, 1).to(DEV)       # non-contiguous
+    yt, _ = rwn.rmsnorm_fwd(xt, inp["weight"].to(DEV), wl.eps)
+    ref, _ = rwn.rmsnorm_fwd(xt.contiguous(), inp["weight"].to(DEV), wl.eps)
+    assert torch.equal(yt, ref)
+    o = gc.oracle_run("rmsnorm", inp, wl.eps, grads=False)
+    tol.assert_reports([tol.compare("rmsnorm.y", y4.reshape(-1, 128), o["y"], o["y_scale"], torch.bfloat16,
+                                    alt=o["y_alt"])])
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_empty_input(layer):
+    wl = workloads.small(layer, 0, 64, "bf16", "f32")
+    inp = {k: v.to(DEV) for k, v in workloads.make_inputs(wl).items()}
+    g = gc.gpu_run(layer, inp, wl.eps)
+    torch.cuda.synchronize()
+    assert g["y"].numel() == 0 and g["dx"].numel() == 0
+    for k in ("dgamma", "dbeta", "dalpha", "dweight"):
+        if g.get(k) is not None:
+            assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+# ------------------------------------------------------------------------ determinism
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_backward_is_bitwise_reproducible(layer):
+    for (M, N, xdt) in [(401408, 24, "f32"), (8192, 128, "bf16"), (4099, 2048, "bf16"), (2049, 1025, "bf16")]:
+        wl = workloads.small(layer, M, N, xdt, "f32", seed=1)
+        _banner(wl, "determinism")
+        inp = {k: v.to(DEV) for k, v in workloads.make_inputs(wl, DEV).items()}
+        a = gc.gpu_run(layer, inp, wl.eps)
+        b = gc.gpu_run(layer, inp, wl.eps)
+        for k in a:
+            if a[k] is not None:
+                assert torch.equal(a[k].view(torch.uint8) if a[k].dtype == torch.bfloat16 else a[k],
+                                   b[k].view(torch.uint8) if b[k].dtype == torch.bfloat16 else b[k]), (wl.name, k)
+
+
+# ------------------------------------------------------------------------ DyT alpha edges
+
+@pytest.mark.parametrize("alpha", [math.inf, 0.0])
+@pytest.mark.parametrize("N", [32, 128, 256])
+def test_dyt_alpha_edges_full_rows(alpha, N):
+    """alpha = +inf and 0 at M = 1,048,573 (prime, above 65,535): finite gradients, matching
+    the oracle.  Padded rows of the last tile must not poison the sums."""
+    wl = workloads.WORKLOADS[f"dyt_bf16_1048573x{N}"].with_(alpha=alpha)
+    _banner(wl.name, "alpha", alpha)
+    inp = workloads.make_inputs(wl, DEV)
+    if alpha == math.inf:
+        assert torch.count_nonzero(inp["x"] == 0).item() == 0
+    rows = gc.sample_rows(wl.M)
+    reps = gc.check_workload(wl, DEV, rows=rows, inputs=inp)
+    g = gc.gpu_run("dyt", inp, wl.eps)
+    for k in ("dalpha", "dgamma", "dbeta"):
+        assert torch.isfinite(g[k]).all(), k
+    if alpha == math.inf:
+        assert g["dalpha"].item() == 0.0
+    tol.assert_reports(reps)
+
+
+# ----------------------------------------------------------------- full-size workloads
+
+FULL = [n for n in workloads.WORKLOADS]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    """Every workload at its real size, in the launch configuration the benchmark times:
+    y/dx/stats on sampled rows (first, last, tile boundaries, random), parameter gradients
+    over all M rows."""
+    wl = workloads.WORKLOADS[name]
+    _banner(name)
+    rows = gc.sample_rows(wl.M, k=24)
+    reps = gc.check_workload(wl, DEV, rows=rows, on_gpu_inputs=True)
+    tol.assert_reports(reps)
