@@ -250,8 +250,17 @@ static void ln_row_stats(const void* x, int xdt, int64_t i, int64_t N, double ep
     *rstd_out = 1.0 / sqrt(v + eps);
 }
 
+/* Mean of |x| over row i: the magnitude sum of the terms of mu. */
+static double row_abs_mean(const void* x, int xdt, int64_t i, int64_t N) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j) s += fabs(load_elem(x, xdt, i * N + j));
+    return s / (double)N;
+}
+
 /* [LN] (torch.nn.LayerNorm reading).  xhat = (x - mu) * rstd; y = xhat * gamma + beta.
- * y_scale = |xhat * gamma| + |beta|.  mean/rstd (may be NULL) receive mu and rstd. */
+ * y_scale sums the magnitudes of every term of y expanded through mu = sum_j x_j / N:
+ * rstd * |gamma| * (|x| + sum_j |x_j| / N) + |beta|.  mean/rstd (may be NULL) receive mu and
+ * rstd. */
 int oracle_layernorm_fwd(int64_t M, int64_t N, const void* x, int xdt, const void* gamma,
                          const void* beta, int pdt, double eps, double* y, double* y_scale,
                          double* mean, double* rstd) {
@@ -262,11 +271,13 @@ int oracle_layernorm_fwd(int64_t M, int64_t N, const void* x, int xdt, const voi
         ln_row_stats(x, xdt, i, N, eps, &mu, &r);
         if (mean) mean[i] = mu;
         if (rstd) rstd[i] = r;
+        const double am = row_abs_mean(x, xdt, i, N);
         for (int64_t j = 0; j < N; ++j) {
-            double xh = (load_elem(x, xdt, i * N + j) - mu) * r;
+            double xv = load_elem(x, xdt, i * N + j);
+            double xh = (xv - mu) * r;
             double g = load_elem(gamma, pdt, j), b = load_elem(beta, pdt, j);
             if (y) y[i * N + j] = xh * g + b;
-            if (y_scale) y_scale[i * N + j] = fabs(xh * g) + fabs(b);
+            if (y_scale) y_scale[i * N + j] = r * fabs(g) * (fabs(xv) + am) + fabs(b);
         }
     }
     return 0;
@@ -293,8 +304,11 @@ static void ln_bwd_terms(const void* vctx, int64_t i, double* terms) {
 
 /* [LN] backward, statistics recomputed from x in double (the GPU's saved stats are not read).
  * With g = dy * gamma, c1 = mean_j(g), c2 = mean_j(g * xhat):
- *   dx       = rstd * (g - c1 - xhat * c2)   dx_scale = rstd * (|g| + |c1| + |xhat * c2|)
- *   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij  (+ magnitude sums). */
+ *   dx       = rstd * (g - c1 - xhat * c2)
+ *   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij  (+ magnitude sums).
+ * dx_scale sums the magnitudes of every term of dx expanded through the row means:
+ * with m = rstd * (|x| + mean_j |x_j|) (the magnitude of xhat's terms),
+ * rstd * (|g| + mean_j |g_j| + m * mean_j |g_j| m_j). */
 int oracle_layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
                          const void* gamma, int pdt, double eps, double* dx, double* dx_scale,
                          double* dgamma, double* dbeta, double* dgamma_scale, double* dbeta_scale) {
@@ -304,20 +318,27 @@ int oracle_layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, in
         for (int64_t i = 0; i < M; ++i) {
             double mu, r;
             ln_row_stats(x, xdt, i, N, eps, &mu, &r);
-            double c1 = 0.0, c2 = 0.0;
+            const double am = row_abs_mean(x, xdt, i, N);
+            double c1 = 0.0, c2 = 0.0, a1 = 0.0, a2 = 0.0;
             for (int64_t j = 0; j < N; ++j) {
+                double xv = load_elem(x, xdt, i * N + j);
                 double g = load_elem(dy, xdt, i * N + j) * load_elem(gamma, pdt, j);
-                double xh = (load_elem(x, xdt, i * N + j) - mu) * r;
+                double xh = (xv - mu) * r;
                 c1 += g;
                 c2 += g * xh;
+                a1 += fabs(g);
+                a2 += fabs(g) * r * (fabs(xv) + am);
             }
             c1 /= (double)N;
             c2 /= (double)N;
+            a1 /= (double)N;
+            a2 /= (double)N;
             for (int64_t j = 0; j < N; ++j) {
+                double xv = load_elem(x, xdt, i * N + j);
                 double g = load_elem(dy, xdt, i * N + j) * load_elem(gamma, pdt, j);
-                double xh = (load_elem(x, xdt, i * N + j) - mu) * r;
+                double xh = (xv - mu) * r;
                 if (dx) dx[i * N + j] = r * (g - c1 - xh * c2);
-                if (dx_scale) dx_scale[i * N + j] = r * (fabs(g) + fabs(c1) + fabs(xh * c2));
+                if (dx_scale) dx_scale[i * N + j] = r * (fabs(g) + a1 + r * (fabs(xv) + am) * a2);
             }
         }
     }
@@ -412,7 +433,8 @@ static void rms_bwd_terms(const void* vctx, int64_t i, double* terms) {
 
 /* [RMS] Semantics.  g = round_xdt(round_arith(dy * w)) (the float32 product, rounded to the
  * input dtype as autograd rounds the gradient of the normalized value); h = x * r (unrounded);
- * c = mean_j(g * h); dx = r * (g - h * c); dx_scale = r * (|g| + |h * c|).
+ * c = mean_j(g * h); dx = r * (g - h * c); dx_scale = r * (|g| + |h| * mean_j |g_j h_j|), the
+ * magnitudes of every term of dx expanded through c.
  * dw_j = sum_i round_wdt(dy_ij * n_ij) (+ magnitude sum). */
 int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
                        const void* w, int wdt, double eps, double* dx, double* dx_scale,
@@ -422,17 +444,19 @@ int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int 
 #pragma omp parallel for schedule(static)
         for (int64_t i = 0; i < M; ++i) {
             double r = rms_row_rstd(x, xdt, i, N, eps);
-            double c = 0.0;
+            double c = 0.0, a = 0.0;
             for (int64_t j = 0; j < N; ++j) {
                 double g = round_to(xdt, round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j)));
                 c += g * load_elem(x, xdt, i * N + j) * r;
+                a += fabs(g * load_elem(x, xdt, i * N + j) * r);
             }
             c /= (double)N;
+            a /= (double)N;
             for (int64_t j = 0; j < N; ++j) {
                 double g = round_to(xdt, round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j)));
                 double h = load_elem(x, xdt, i * N + j) * r;
                 if (dx) dx[i * N + j] = r * (g - h * c);
-                if (dx_scale) dx_scale[i * N + j] = r * (fabs(g) + fabs(h * c));
+                if (dx_scale) dx_scale[i * N + j] = r * (fabs(g) + fabs(h) * a);
             }
         }
     }
