@@ -85,7 +85,7 @@ def _bind(lib):
     lib.oracle_layernorm_fwd.argtypes = [i64, i64, vp, ci, vp, vp, ci, cd, dp, dp, dp, dp]
     lib.oracle_layernorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp, dp]
     lib.oracle_rmsnorm_fwd.argtypes = [i64, i64, vp, ci, vp, ci, cd, dp, dp, dp, dp]
-    lib.oracle_rmsnorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp]
     for f in ("oracle_dyt_fwd", "oracle_dyt_bwd", "oracle_layernorm_fwd", "oracle_layernorm_bwd",
               "oracle_rmsnorm_fwd", "oracle_rmsnorm_bwd"):
         getattr(lib, f).restype = ci
@@ -213,11 +213,11 @@ def rmsnorm_bwd(x, dy, weight, eps: float, want_dx: bool = True) -> Dict[str, np
     M, N = x.shape
     dx = _out((M, N)) if want_dx else None
     dxs = _out((M, N)) if want_dx else None
-    dw, dws = _out(N), _out(N)
+    dw, dws, dwl = _out(N), _out(N), _out(N)
     _check(lib.oracle_rmsnorm_bwd(M, N, x.data_ptr(), dy.data_ptr(), _DT[x.dtype],
                                   weight.data_ptr(), _DT[weight.dtype], float(eps), _p(dx), _p(dxs),
-                                  _p(dw), _p(dws)), "oracle_rmsnorm_bwd")
-    out = {"dweight": dw, "dweight_scale": dws}
+                                  _p(dw), _p(dws), _p(dwl)), "oracle_rmsnorm_bwd")
+    out = {"dweight": dw, "dweight_scale": dws, "dweight_slack": dwl}
     if want_dx:
         out.update(dx=dx, dx_scale=dxs)
     return out

@@ -421,13 +421,20 @@ typedef struct {
 /* Column terms of row i: round_wdt(round_arith(dy * n)) with n = round_xdt(x * rstd).  The
  * weight gradient is formed in the weight's dtype, so a bfloat16 weight rounds each product
  * to bfloat16 before the column sum ([RMS] Semantics); a float32 weight keeps the float32
- * product (exact for bf16 * bf16). */
+ * product (exact for bf16 * bf16).  Columns [N, 2N) receive |term(n_alt) - term(n)|, where
+ * n_alt is the other rounding of h that a float32 computation may also reach (see
+ * rounding_alternative): the slack the column sum may legitimately carry. */
 static void rms_bwd_terms(const void* vctx, int64_t i, double* terms) {
     const rms_ctx* c = (const rms_ctx*)vctx;
     double r = rms_row_rstd(c->x, c->xdt, i, c->N, c->eps);
     for (int64_t j = 0; j < c->N; ++j) {
-        double n = round_to(c->xdt, load_elem(c->x, c->xdt, i * c->N + j) * r);
-        terms[j] = round_to(c->wdt, round_arith(c->xdt, load_elem(c->dy, c->xdt, i * c->N + j) * n));
+        double h = load_elem(c->x, c->xdt, i * c->N + j) * r;
+        double n = round_to(c->xdt, h);
+        double g = load_elem(c->dy, c->xdt, i * c->N + j);
+        double t = round_to(c->wdt, round_arith(c->xdt, g * n));
+        double ta = round_to(c->wdt, round_arith(c->xdt, g * rounding_alternative(h, n, c->xdt)));
+        terms[j] = t;
+        terms[c->N + j] = fabs(ta - t);
     }
 }
 
@@ -435,10 +442,11 @@ static void rms_bwd_terms(const void* vctx, int64_t i, double* terms) {
  * input dtype as autograd rounds the gradient of the normalized value); h = x * r (unrounded);
  * c = mean_j(g * h); dx = r * (g - h * c); dx_scale = r * (|g| + |h| * mean_j |g_j h_j|), the
  * magnitudes of every term of dx expanded through c.
- * dw_j = sum_i round_wdt(dy_ij * n_ij) (+ magnitude sum). */
+ * dw_j = sum_i round_wdt(dy_ij * n_ij) (+ magnitude sum; dw_slack_j = sum_i of the change of
+ * the term under the other admissible rounding of n, may be NULL). */
 int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
                        const void* w, int wdt, double eps, double* dx, double* dx_scale,
-                       double* dw, double* dw_scale) {
+                       double* dw, double* dw_scale, double* dw_slack) {
     if (M < 0 || N < 1) return -1;
     if (dx || dx_scale) {
 #pragma omp parallel for schedule(static)
@@ -460,9 +468,20 @@ int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int 
             }
         }
     }
-    if (dw || dw_scale) {
+    if (dw || dw_scale || dw_slack) {
         rms_ctx c = {N, x, dy, xdt, wdt, eps};
-        if (column_sums(&c, rms_bwd_terms, M, N, dw, dw_scale) != 0) return -2;
+        double* s = (double*)malloc((size_t)(2 * N) * sizeof(double));
+        double* a = (double*)malloc((size_t)(2 * N) * sizeof(double));
+        if (!s || !a || column_sums(&c, rms_bwd_terms, M, 2 * N, s, a) != 0) {
+            free(s); free(a);
+            return -2;
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            if (dw) dw[j] = s[j];
+            if (dw_scale) dw_scale[j] = a[j];
+            if (dw_slack) dw_slack[j] = s[N + j];
+        }
+        free(s); free(a);
     }
     return 0;
 }

@@ -160,11 +160,12 @@ rwn_status workspace_size(int layer, int64_t M, int64_t N, rwn_dtype xdt, size_t
     // The plan depends on the operands' address modulo 16; size for the largest.
     const int esz = xdt == RWN_F32 ? 4 : 2;
     int64_t grid = 0;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != RWN_OK) return st;
     for (int mis = 0; mis < 16; mis += esz) {
         Plan p;
-        st = plan_for(fn, layer, true, M, N, xdt, mis, &p);
-        if (st != RWN_OK) return st;
-        if (p.grid > grid) grid = p.grid;
+        // a misalignment with no plan is rejected by the backward itself
+        if (make_plan(layer, true, M, N, (int)xdt, mis, cus, &p) && p.grid > grid) grid = p.grid;
     }
     *bytes = (size_t)grid * (size_t)partial_cols(layer, N) * sizeof(float);
     return ok();

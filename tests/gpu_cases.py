@@ -97,7 +97,8 @@ def compare(layer: str, gpu: Dict[str, torch.Tensor], ora: Dict[str, np.ndarray]
         names = {"dyt": ["dgamma", "dbeta", "dalpha"], "layernorm": ["dgamma", "dbeta"], "rmsnorm": ["dweight"]}[layer]
         for n in names:
             if gpu.get(n) is not None:
-                reps.append(tol.compare_param(f"{layer}.{n}", gpu[n], ora[n], ora[n + "_scale"], pdt))
+                reps.append(tol.compare_param(f"{layer}.{n}", gpu[n], ora[n], ora[n + "_scale"], pdt,
+                                              slack=ora.get(n + "_slack")))
     return reps
 
 

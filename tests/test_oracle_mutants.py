@@ -35,7 +35,8 @@ MUTANTS = [
     ("rms_n_not_rounded", "            double n = round_to(xdt, h);\n", "            double n = h;\n"),
     ("rms_g_not_rounded", "double g = round_to(xdt, round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j)));\n                double h",
      "double g = round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j));\n                double h"),
-    ("rms_dw_term_not_rounded", "terms[j] = round_to(c->wdt, round_arith(", "terms[j] = (("),
+    ("rms_dw_term_not_rounded", "double t = round_to(c->wdt, round_arith(c->xdt, g * n));",
+     "double t = round_arith(c->xdt, g * n);"),
     ("rms_dx_sign", "if (dx) dx[i * N + j] = r * (g - h * c);", "if (dx) dx[i * N + j] = r * (g + h * c);"),
     ("rms_sum_not_mean", "return 1.0 / sqrt(s / (double)N + eps);", "return 1.0 / sqrt(s + eps);"),
     ("colsum_drops_block_tail", "int64_t i1 = (b + 1) * ORA_ROW_BLOCK < M ? (b + 1) * ORA_ROW_BLOCK : M;",

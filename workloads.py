@@ -149,7 +149,13 @@ def make_inputs(wl: Workload, device="cpu", seed_offset: int = 0) -> Dict[str, t
         u = torch.rand((wl.M, wl.N), generator=_gen(device, s + 1), device=device)
         x = torch.where(u < wl.outlier_frac, x * 10.0, x)
         del u
-    out = {"x": x.to(xdt)}
+    x = x.to(xdt)
+    if wl.layer == "dyt" and math.isinf(wl.alpha):
+        # With alpha = +inf an exact zero is a true NaN (tanh(inf * 0)); the generators can emit
+        # 0.0 (about once per 2^24 draws), so such elements are moved to the smallest normal.
+        tiny = torch.finfo(torch.float32).tiny
+        x = torch.where(x == 0, torch.full_like(x, tiny), x)
+    out = {"x": x}
     del x
     out["dy"] = _normal((wl.M, wl.N), 0.0, wl.dy_std, s + 2, device).to(xdt)
     if wl.layer == "dyt":
