@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--sweep", default=None, help="also time every workload and write JSON lines here")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None, help="comma-separated substrings: sweep only matching workloads")
+    ap.add_argument("--no-trace", action="store_true", help="time without per-kernel HIP events")
     return ap.parse_args()
 
 
@@ -67,7 +69,7 @@ def kernel_bytes(wl, kernel: str) -> int:
     return 0
 
 
-def time_workload(wl, steps: int, warmup: int):
+def time_workload(wl, steps: int, warmup: int, trace: bool = True):
     import torch
     import workloads
     import row_wise_normalization_dyt_amd as rwn
@@ -85,7 +87,8 @@ def time_workload(wl, steps: int, warmup: int):
         sets[i % nsets].step()
     torch.cuda.synchronize()
 
-    rwn.trace_begin(3 * steps + 8)
+    if trace:
+        rwn.trace_begin(3 * steps + 8)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -96,10 +99,10 @@ def time_workload(wl, steps: int, warmup: int):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    trace = rwn.trace_end(3 * steps + 8)
+    events = rwn.trace_end(3 * steps + 8) if trace else []
     ms_total = t0.elapsed_time(t1)
     per = {}
-    for name, ms in trace:
+    for name, ms in events:
         tot, cnt = per.get(name, (0.0, 0))
         per[name] = (tot + ms, cnt + 1)
     kernels = {k: {"avg_ms": t / c, "launches": c, "total_ms": t} for k, (t, c) in per.items()}
@@ -187,6 +190,7 @@ def main():
     traffic_db = json.load(open(tdb_path)) if os.path.exists(tdb_path) else {}
 
     r = time_workload(wl, args.steps, args.warmup)
+    untraced = time_workload(wl, args.steps, args.warmup, trace=False)["ms_per_step"]
     byts = wl.algorithmic_bytes()["total"]
     value = byts / (r["ms_per_step"] * 1e-3) / 1e9
     line = {
@@ -197,6 +201,7 @@ def main():
                    "param_dtype": wl.pdt, "bytes_per_step": byts,
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
                    "rotating_input_sets": r["nsets"],
+                   "ms_per_step_untraced": round(untraced, 5),
                    "kernel_avg_ms": {k: round(v["avg_ms"], 5) for k, v in r["kernels"].items()},
                    "copy_probe_GBps": copy_probe_gbps()},
         "roofline": roofline(wl, r["kernels"], traffic_db),
@@ -207,16 +212,20 @@ def main():
 
     if args.sweep:
         with open(args.sweep, "w") as f:
+            only = args.only.split(",") if args.only else None
             for n, w in workloads.WORKLOADS.items():
+                if only and not any(o in n for o in only):
+                    continue
                 del r
                 torch.cuda.empty_cache()
-                r = time_workload(w, max(10, min(args.steps, 100)), 5)
+                r = time_workload(w, max(10, min(args.steps, 100)), 5, trace=not args.no_trace)
                 b = w.algorithmic_bytes()
                 v = b["total"] / (r["ms_per_step"] * 1e-3) / 1e9
-                rec = {"workload": n, "GBps": round(v, 1), "pct_of_peak": round(100 * v / HBM_PEAK_GBPS, 2),
+                rec = {"workload": n, "env": {k: v for k, v in os.environ.items() if k.startswith("RWN_")},
+                       "GBps": round(v, 1), "pct_of_peak": round(100 * v / HBM_PEAK_GBPS, 2),
                        "ms_per_step": round(r["ms_per_step"], 5), "bytes_per_step": b["total"],
                        "kernels": {k: round(x["avg_ms"], 5) for k, x in r["kernels"].items()},
-                       "roofline": roofline(w, r["kernels"], traffic_db)}
+                       "roofline": roofline(w, r["kernels"], traffic_db) if r["kernels"] else None}
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 print("sweep", json.dumps(rec), file=sys.stderr, flush=True)

@@ -39,8 +39,9 @@
  * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16
  *            elements) spread over at most 1024 threads; when N is not a multiple of the chunk
  *            or the operands are not 16-byte aligned a row may straddle one more chunk, so
- *            those calls take N <= 16381 (float32) / 16377 (bfloat16) and otherwise return
- *            RWN_ERR_UNSUPPORTED.
+ *            those LayerNorm/RMSNorm calls take N <= 16381 (float32) / 16377 (bfloat16) and
+ *            otherwise return RWN_ERR_UNSUPPORTED.  DyT splits wide rows into column blocks
+ *            and takes every N up to 16384.
  */
 #ifndef RWNORM_H
 #define RWNORM_H
@@ -156,10 +157,11 @@ int rwn_trace_end(float* ms, int* tags, int capacity);
 rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Launch plan the library chooses for an entry point (introspection for tests and tuning).
- * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 9 integers to out:
+ * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 12 integers to out:
  * {mode (0 aligned vectors, 1 shifted vectors, 2 scalar), chunks per thread, rows per thread,
  *  threads per row, row slots per workgroup, workgroup size, workgroups, row tiles,
- *  elements per chunk}.  misalign_bytes is the common address of x/y/dy/dx modulo 16; cus is
+ *  elements per chunk, row tiles per workgroup (0 when strided), strided (1: workgroup w
+ *  visits tiles w, w + workgroups / column blocks, ...), column blocks per row}.  misalign_bytes is the common address of x/y/dy/dx modulo 16; cus is
  * the compute-unit count to plan for (0: query the current device). */
 rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
                     int misalign_bytes, int cus, int64_t* out);

@@ -6,26 +6,40 @@
 
 namespace rwn {
 
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+
 static int64_t next_pow2(int64_t v) {
     int64_t p = 1;
     while (p < v) p <<= 1;
     return p;
 }
 
-// Tuning override, read once: RWN_WG_PER_CU=<k> sets the workgroups per CU of the row kernels.
-// Changing it changes the reduction order (and so the low bits of parameter gradients).
-static int env_wg_per_cu() {
-    static int v = [] {
-        const char* s = getenv("RWN_WG_PER_CU");
-        int k = s ? atoi(s) : 0;
-        return (k >= 1 && k <= 32) ? k : 0;
-    }();
-    return v;
+// Tuning overrides, read once (each changes the launch plan, and with it the reduction order
+// and so the low bits of parameter gradients):
+//   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4)
+//   RWN_WINDOW_KB           target bytes of one tensor touched per grid-stride step
+//   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
+//   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
+//   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
+//                           of striding (fwd stays strided)
+static int env_int(const char* name, int lo, int hi, int dflt) {
+    const char* s = getenv(name);
+    if (!s) return dflt;
+    int k = atoi(s);
+    return (k >= lo && k <= hi) ? k : dflt;
 }
 
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misalign_bytes,
                int cus, Plan* out) {
-    (void)layer;
+    static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
+    static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 1);
+    static const int window_kb = env_int("RWN_WINDOW_KB", 64, 1 << 20, 2048);
+    static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
+    static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
+    static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
     Plan p;
     p.M = M;
     p.N = N;
@@ -49,21 +63,39 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         }
     }
     const int v_elems = p.mode == MODE_SCALAR ? 1 : V;
-    if (chunks <= 64) {
+    if (layer == LAYER_DYT && chunks > 64 && p.mode != MODE_SCALAR) {
+        // DyT has no row reduction: wide rows are cut into ncb column blocks of W <= 8 waves,
+        // one chunk per lane (its per-element state is the largest of the three layers).
+        // Fewest idle lanes, ties to the widest block.
+        int64_t best = -1;
+        for (int w = 8; w >= 1; --w) {
+            const int64_t ncb = (chunks + 64 * w - 1) / (64 * w);
+            const int64_t waste = ncb * 64 * w - chunks;
+            if (best < 0 || waste < best) {
+                best = waste;
+                p.tpr = 64 * w;
+                p.ncb = (int)ncb;
+            }
+        }
+        p.cpt = 1;
+    } else if (chunks <= 64) {
         // Narrow rows: a power-of-two group of lanes per row, several rows per wave.
         p.tpr = (int)next_pow2(chunks);
         p.cpt = 1;
     } else {
-        // Wide rows: W waves per row, CPT chunks per lane; least idle lanes, then CPT = 2.
-        const int cpt_max = (xdt == DT_F32 || p.mode == MODE_SCALAR) ? 4 : 2;
+        // Wide rows: W waves per row, CPT chunks per lane.  Fewest idle lanes; ties go to
+        // CPT = 1, then 4, for DyT (no row reduction, and its per-element state is the largest,
+        // so it wants the larger register budget of <= 8-wave rows) and to CPT = 2 otherwise
+        // (fewer waves to combine per row).  Wave limits follow the kernels' launch bounds.
         int best_cpt = 0, best_w = 0;
         int64_t best_waste = -1;
-        const int order[3] = {2, 4, 1};
+        const int order_dyt[3] = {1, 4, 2}, order_norm[3] = {2, 4, 1};
+        const int* order = layer == LAYER_DYT ? order_dyt : order_norm;
         for (int oi = 0; oi < 3; ++oi) {
             const int cpt = order[oi];
-            if (cpt > cpt_max) continue;
+            const int wmax = (cpt == 1 || (cpt == 4 && esz == 2)) ? 8 : 16;
             const int64_t w = (chunks + 64 * cpt - 1) / (64 * cpt);
-            if (w > 16) continue;
+            if (w > wmax) continue;
             const int64_t waste = w * 64 * cpt - chunks;
             if (best_waste < 0 || waste < best_waste) {
                 best_waste = waste;
@@ -75,41 +107,93 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         p.cpt = best_cpt;
         p.tpr = 64 * best_w;
     }
-    p.rt = (p.mode == MODE_ALIGNED && p.cpt == 1 && p.tpr <= 64) ? 4 : 1;
-    // SHIFTED rows each have their own shift, so a workgroup holds a single row slot.
-    p.rpp = (p.mode == MODE_SHIFTED || p.tpr >= 256) ? 1 : 256 / p.tpr;
+    const bool narrow_aligned = p.mode == MODE_ALIGNED && p.cpt == 1 && p.tpr <= 64;
+    p.rt = narrow_aligned ? (backward ? bwd_rt : fwd_rt) : 1;
+    if (p.rt == 3) p.rt = 2;
+
+    // Row slots: narrow rows fill 256-thread workgroups; wide rows use wide_block threads.
+    // SHIFTED slots each carry their own shift, so a strided SHIFTED workgroup has one slot.
+    const bool blocked = backward && blocked_k > 0 && p.ncb == 1;
+    if (p.mode == MODE_SHIFTED) {
+        p.rpp = (blocked && (int64_t)p.tpr * V <= 1024) ? V : 1;
+    } else {
+        const int target = p.tpr <= 64 ? 256 : wide_block;
+        p.rpp = p.tpr >= target ? 1 : target / p.tpr;
+    }
+    if (p.ncb > 1 && p.mode == MODE_SHIFTED) p.rpp = 1;
+    // Keep to the kernel shape's launch bound (tpr itself always fits: see the wave limits).
+    const int maxb = max_block(p.rt, p.cpt, esz);
+    if (p.tpr * p.rpp > maxb) p.rpp = maxb / p.tpr > 0 ? maxb / p.tpr : 1;
+    if (p.mode == MODE_SHIFTED && p.rpp > 1 && p.rpp % V) p.rpp = 1;
     p.block = p.tpr * p.rpp;
+    if (p.block > maxb) return false;
     const int64_t rows_per_tile = (int64_t)p.rpp * p.rt;
     p.ntiles = (M + rows_per_tile - 1) / rows_per_tile;
-    int wg_per_cu = env_wg_per_cu();
-    if (wg_per_cu == 0) wg_per_cu = (int)(1024 / p.block) > 1 ? (int)(1024 / p.block) : 1;
-    if (wg_per_cu > 16) wg_per_cu = 16;
-    int64_t grid = (int64_t)cus * wg_per_cu;
-    if (grid >= p.ntiles) {
-        grid = p.ntiles;              // one tile per workgroup
+
+    if (blocked) {
+        p.kt = blocked_k;
+        p.grid = (p.ntiles + p.kt - 1) / p.kt;
     } else {
-        grid -= grid % 8;             // SHIFTED: grid * rpp must be a multiple of V (<= 8)
-        if (grid < 8) grid = 8;
+        // Persistent grid-stride.  HBM streams best when the bytes in flight come from a
+        // compact address window: size the grid so one stride step covers ~window_kb of each
+        // tensor, but never below min_waves resident waves per CU.  With ncb column blocks the
+        // grid is ncb workgroups per tile stride.
+        p.strided = 1;
+        const double tile_bytes = (double)rows_per_tile * (double)N * esz;
+        int64_t gt = (int64_t)((double)window_kb * 1024.0 / tile_bytes);
+        const int64_t waves_per_wg = (p.block + 63) / 64;
+        const int64_t gmin = ((int64_t)cus * min_waves + waves_per_wg * p.ncb - 1) / (waves_per_wg * p.ncb);
+        if (gt < gmin) gt = gmin;
+        if (gt * p.ncb > (int64_t)cus * 32) gt = (int64_t)cus * 32 / p.ncb;
+        if (gt >= p.ntiles) {
+            gt = p.ntiles;                     // one tile per workgroup
+        } else {
+            gt -= gt % 8;                      // SHIFTED: the tile stride * rpp must be a multiple of V
+            if (gt < 8) gt = 8;
+        }
+        p.grid = gt * p.ncb;
+        p.kt = 0;
     }
-    p.grid = grid;
-    p.lds_bytes = (backward && p.rpp > 1) ? (size_t)p.cpt * v_elems * p.block * sizeof(float) : 0;
+    if (backward) {
+        // Partials column-major when rows are short (stage 2 then reads each column
+        // contiguously), row-major when wide (stage 1 then writes each row contiguously).
+        const int64_t ng = partial_cols(layer, N, p.ncb);
+        if (ng <= 1024) {
+            p.ws_rs = 1;
+            p.ws_cs = p.partial_rows();
+        } else {
+            p.ws_rs = ng;
+            p.ws_cs = 1;
+        }
+        if (p.rpp > 1) {
+            int64_t e = (int64_t)p.cpt * v_elems * p.block;
+            if (p.mode == MODE_SHIFTED && N > e) e = N;
+            p.lds_bytes = (size_t)e * sizeof(float);
+        }
+    }
     *out = p;
     return true;
 }
 
-hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t N,
-                            void* out0, void* out1, void* out2, hipStream_t s) {
+hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
+                            int64_t N, void* out0, void* out1, void* out2, hipStream_t s) {
     const int block = 512;
-    const int cb = ng <= 64 ? 8 : (ng <= 1024 ? 16 : 64);
+    // Lanes per column: enough that each lane adds ~8 partial rows (column-major partials) or
+    // ~16 (row-major, where lanes of one column are not contiguous).
+    const int64_t per = cs == 1 ? 16 : 8;
+    int64_t L = next_pow2((P + per - 1) / per);
+    const int64_t lmax = cs == 1 ? 64 : 512;
+    if (L < 8) L = 8;
+    if (L > lmax) L = lmax;
+    const int cb = (int)(block / L);
     const unsigned grid = (unsigned)((ng + cb - 1) / cb);
     if (pdt == DT_F32) {
-        hipLaunchKernelGGL(colreduce_kernel<float>, dim3(grid), dim3(block), 0, s, ws, P, ng, N, cb,
-                           (float*)out0, (float*)out1, (float*)out2);
+        return launch(colreduce_kernel<float>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
+                      (float*)out0, (float*)out1, (float*)out2);
     } else {
-        hipLaunchKernelGGL(colreduce_kernel<bf16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, N, cb,
-                           (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
+        return launch(colreduce_kernel<bf16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
+                      (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
     }
-    return hipGetLastError();
 }
 
 // Bandwidth probe: 16-byte vector copy, grid-stride.
@@ -125,9 +209,8 @@ hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream
     int64_t grid = (n16 + 255) / 256;
     if (grid > 65536) grid = 65536;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const f32x4*)src,
-                       (f32x4*)dst, n16);
-    return hipGetLastError();
+    return launch(copy_probe_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const f32x4*)src,
+                  (f32x4*)dst, n16);
 }
 
 }  // namespace rwn

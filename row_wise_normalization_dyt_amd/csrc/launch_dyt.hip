@@ -11,11 +11,12 @@ hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
         return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
-            hipLaunchKernelGGL((dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>),
+            constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
+            if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+            return launch(dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)alpha, (const PT*)gamma, (const PT*)beta, (T*)y, g);
-            return hipGetLastError();
         });
     });
 }
@@ -24,16 +25,16 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
                           const void* alpha, const void* gamma, void* dx, float* ws,
                           hipStream_t s) {
     const Geom g = make_geom(p);
-    const int64_t ng = partial_cols(LAYER_DYT, p.N);
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
         return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
-            hipLaunchKernelGGL((dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>),
+            constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
+            if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+            return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
-                               (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, ng, g);
-            return hipGetLastError();
+                               (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, g);
         });
     });
 }

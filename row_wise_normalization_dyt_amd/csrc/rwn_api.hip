@@ -122,11 +122,11 @@ hipError_t traced(int tag, hipStream_t s, F&& launch) {
     Trace& t = g_trace;
     if (!t.on || t.used >= t.cap) return launch();
     TraceEntry& e = t.ev[t.used];
-    hipError_t r = hipEventRecord(e.a, s);
-    if (r != hipSuccess) return r;
-    r = launch();
-    if (r != hipSuccess) return r;
-    r = hipEventRecord(e.b, s);
+    // The launch records its own start/stop timestamps (see rwn::launch).
+    (void)s;
+    launch_events() = LaunchEvents{e.a, e.b};
+    hipError_t r = launch();
+    launch_events() = LaunchEvents{};
     if (r != hipSuccess) return r;
     e.tag = tag;
     ++t.used;
@@ -159,20 +159,22 @@ rwn_status workspace_size(int layer, int64_t M, int64_t N, rwn_dtype xdt, size_t
     }
     // The plan depends on the operands' address modulo 16; size for the largest.
     const int esz = xdt == RWN_F32 ? 4 : 2;
-    int64_t grid = 0;
+    size_t most = 0;
     int cus = 0;
     if ((st = device_cus(&cus)) != RWN_OK) return st;
     for (int mis = 0; mis < 16; mis += esz) {
         Plan p;
         // a misalignment with no plan is rejected by the backward itself
-        if (make_plan(layer, true, M, N, (int)xdt, mis, cus, &p) && p.grid > grid) grid = p.grid;
+        if (!make_plan(layer, true, M, N, (int)xdt, mis, cus, &p)) continue;
+        const size_t need = (size_t)p.partial_rows() * (size_t)partial_cols(layer, N, p.ncb) * sizeof(float);
+        if (need > most) most = need;
     }
-    *bytes = (size_t)grid * (size_t)partial_cols(layer, N) * sizeof(float);
+    *bytes = most;
     return ok();
 }
 
 rwn_status check_workspace(const char* fn, const Plan& p, int layer, const void* ws, size_t ws_bytes) {
-    const size_t need = (size_t)p.grid * (size_t)partial_cols(layer, p.N) * sizeof(float);
+    const size_t need = (size_t)p.partial_rows() * (size_t)partial_cols(layer, p.N, p.ncb) * sizeof(float);
     if (need == 0) return RWN_OK;
     if (!ws) return fail(RWN_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
     if (ws_bytes < need)
@@ -182,11 +184,11 @@ rwn_status check_workspace(const char* fn, const Plan& p, int layer, const void*
 }
 
 // Stage 2 (also the whole backward when M == 0: P = 0 partial rows give zeros).
-rwn_status finish_bwd(const char* fn, int pdt, const float* ws, int64_t P, int64_t ng, int64_t N,
-                      void* out0, void* out1, void* out2, hipStream_t s) {
+rwn_status finish_bwd(const char* fn, int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs,
+                      int64_t cs, int64_t N, void* out0, void* out1, void* out2, hipStream_t s) {
     if (!out0 && !out1 && !out2) return ok();
     hipError_t e = traced(RWN_K_COLREDUCE, s, [&] {
-        return launch_colreduce(pdt, ws, P, ng, N, out0, out1, out2, s);
+        return launch_colreduce(pdt, ws, P, ng, rs, cs, N, out0, out1, out2, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -228,7 +230,7 @@ RWN_API rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, 
     if (!alpha || !gamma) return fail(RWN_ERR_INVALID_ARG, "%s: alpha and gamma are required", fn);
     hipStream_t s = (hipStream_t)stream;
     const int64_t ng = partial_cols(LAYER_DYT, N);
-    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, N, dgamma, dbeta, dalpha, s);
+    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, ng, 1, N, dgamma, dbeta, dalpha, s);
     const void* ops[3] = {x, dy, dx};
     const char* names[3] = {"x", "dy", "dx"};
     int mis = 0;
@@ -241,7 +243,8 @@ RWN_API rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, 
         return launch_dyt_bwd(p, x_dtype, param_dtype, x, dy, alpha, gamma, dx, ws, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
-    return finish_bwd(fn, param_dtype, ws, p.grid, ng, N, dgamma, dbeta, dalpha, s);
+    return finish_bwd(fn, param_dtype, ws, p.partial_rows(), partial_cols(LAYER_DYT, N, p.ncb), p.ws_rs,
+                      p.ws_cs, N, dgamma, dbeta, dalpha, s);
 }
 
 RWN_API rwn_status dyt_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
@@ -287,7 +290,7 @@ RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void
         return fail(RWN_ERR_INVALID_ARG, "%s: pass both mean and rstd, or neither", fn);
     hipStream_t s = (hipStream_t)stream;
     const int64_t ng = partial_cols(LAYER_LN, N);
-    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, N, dgamma, dbeta, nullptr, s);
+    if (M == 0) return finish_bwd(fn, param_dtype, nullptr, 0, ng, ng, 1, N, dgamma, dbeta, nullptr, s);
     const void* ops[3] = {x, dy, dx};
     const char* names[3] = {"x", "dy", "dx"};
     int mis = 0;
@@ -300,7 +303,7 @@ RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void
         return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
-    return finish_bwd(fn, param_dtype, ws, p.grid, ng, N, dgamma, dbeta, nullptr, s);
+    return finish_bwd(fn, param_dtype, ws, p.partial_rows(), ng, p.ws_rs, p.ws_cs, N, dgamma, dbeta, nullptr, s);
 }
 
 RWN_API rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
@@ -344,7 +347,7 @@ RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* 
     if (!weight) return fail(RWN_ERR_INVALID_ARG, "%s: weight is required", fn);
     hipStream_t s = (hipStream_t)stream;
     const int64_t ng = partial_cols(LAYER_RMS, N);
-    if (M == 0) return finish_bwd(fn, weight_dtype, nullptr, 0, ng, N, dweight, nullptr, nullptr, s);
+    if (M == 0) return finish_bwd(fn, weight_dtype, nullptr, 0, ng, ng, 1, N, dweight, nullptr, nullptr, s);
     const void* ops[3] = {x, dy, dx};
     const char* names[3] = {"x", "dy", "dx"};
     int mis = 0;
@@ -357,7 +360,7 @@ RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* 
         return launch_rms_bwd(p, x_dtype, weight_dtype, x, dy, rstd, weight, eps, dx, ws, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
-    return finish_bwd(fn, weight_dtype, ws, p.grid, ng, N, dweight, nullptr, nullptr, s);
+    return finish_bwd(fn, weight_dtype, ws, p.partial_rows(), ng, p.ws_rs, p.ws_cs, N, dweight, nullptr, nullptr, s);
 }
 
 RWN_API rwn_status rmsnorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {
@@ -457,5 +460,8 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
     out[0] = p.mode; out[1] = p.cpt; out[2] = p.rt; out[3] = p.tpr; out[4] = p.rpp;
     out[5] = p.block; out[6] = p.grid; out[7] = p.ntiles;
     out[8] = p.mode == MODE_SCALAR ? 1 : 16 / esz;
+    out[9] = p.strided ? 0 : p.kt;
+    out[10] = p.strided;
+    out[11] = p.ncb;
     return ok();
 }

@@ -21,29 +21,52 @@
 namespace rwn {
 
 constexpr int kMaxBlock = 1024;
-// Narrow plans (RT > 1) always run 256-thread workgroups; wide plans up to 1024.
-template <int RT> struct MaxBlock { static constexpr int value = RT > 1 ? 256 : kMaxBlock; };
+// Largest workgroup a plan gives each kernel shape (the planner keeps to it): narrow plans
+// (RT > 1) run 256 threads; one chunk per thread, and bf16 with four, at most 8 waves per row
+// (a 256-register budget); otherwise up to 16 waves (128 registers).
+template <typename T, int RT, int CPT> struct MaxBlock {
+    static constexpr int value = RT > 1 ? 256 : (CPT == 1 || (CPT == 4 && sizeof(T) == 2)) ? 512 : kMaxBlock;
+};
+static_assert(MaxBlock<bf16_t, 1, 4>::value == 512 && MaxBlock<float, 1, 4>::value == 1024 &&
+                  MaxBlock<float, 4, 1>::value == 256 && MaxBlock<bf16_t, 1, 2>::value == 1024,
+              "kernel launch bounds must match the planner's max_block()");
 constexpr int kRedFloats = 2 * (kMaxBlock / 64) * 8;   // row_sum buffers: 2 halves x waves x K<=8
 
-// Per-thread setup common to all row kernels.
+// Per-thread setup common to all row kernels: slot/lane, the workgroup's tile range and the
+// thread's column map.
 template <typename T, int MODE, int CPT, int RT>
 struct RowCtx {
     int slot, lane;
+    int cblk;           // column block of this workgroup
+    int64_t wg;         // workgroup index among those sharing cblk (= its partial row)
     int64_t rows_per_tile;
+    int64_t t_begin, t_end, t_step;
     ColMap<T, MODE, CPT> cm;
 
     __device__ __forceinline__ RowCtx(const Geom& g) {
         slot = threadIdx.x / g.tpr;
         lane = threadIdx.x - slot * g.tpr;
+        cblk = (int)(blockIdx.x % g.ncb);
+        wg = blockIdx.x / g.ncb;
         rows_per_tile = (int64_t)g.rpp * RT;
+        if (g.strided) {
+            t_begin = wg;
+            t_end = g.ntiles;
+            t_step = gridDim.x / g.ncb;
+        } else {
+            t_begin = wg * g.kt;
+            t_end = t_begin + g.kt < g.ntiles ? t_begin + g.kt : g.ntiles;
+            t_step = 1;
+        }
         int s = 0;
         if (MODE == MODE_SHIFTED) {
-            // All rows this thread visits differ by a multiple of V (host guarantee), so the
-            // first one fixes the shift.
-            const int64_t r0 = (int64_t)blockIdx.x * rows_per_tile + slot;
+            // Every row this thread visits differs from the first by a multiple of V (the
+            // launcher makes rpp, or the tile stride times rpp, a multiple of V), so the first
+            // row fixes the shift.
+            const int64_t r0 = t_begin * rows_per_tile + slot;
             s = (int)(((int64_t)g.base_shift + r0 * g.N) % ColMap<T, MODE, CPT>::V);
         }
-        cm.init(lane, g.tpr, g.N, s);
+        cm.init(lane, g.tpr, g.N, s, cblk * g.tpr * CPT);
     }
     __device__ __forceinline__ int64_t row(int64_t tile, int u, const Geom& g) const {
         return tile * rows_per_tile + (int64_t)u * g.rpp + slot;
@@ -63,10 +86,10 @@ __device__ __forceinline__ void load_param_or(const PT* __restrict__ p, float df
     }
 }
 
-// Write one gradient's partial row: out[col] = sum over row slots (slot order) of acc.
-// `part` is E * blockDim.x floats of LDS (only used when rpp > 1).
+// Write one gradient's partial row: out[col * cs] = sum over row slots (slot order) of acc.
+// `part` is LDS of max(E * blockDim.x, N) floats (only used when rpp > 1).
 template <typename T, int MODE, int CPT>
-__device__ __forceinline__ void write_partial(float* __restrict__ out, const float* acc,
+__device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t cs, const float* acc,
                                               const ColMap<T, MODE, CPT>& cm, int slot, int lane,
                                               const Geom& g, float* part) {
     constexpr int V = ColMap<T, MODE, CPT>::V;
@@ -76,10 +99,30 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, const flo
         for (int k = 0; k < CPT; ++k)
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                if (cm.valid(k, v, g.N)) out[cm.col0[k] + v] = acc[k * V + v];
+                if (cm.valid(k, v, g.N)) out[(int64_t)(cm.col0[k] + v) * cs] = acc[k * V + v];
         return;
     }
     const int nb = blockDim.x;
+    if (MODE == MODE_SHIFTED) {
+        // Slots hold different column maps: add them into a column-indexed LDS row, one slot
+        // at a time (within a slot every column has one owner).  (Only single-column-block
+        // plans have SHIFTED slots, so the row is all of [0, N).)
+        __syncthreads();
+        for (int64_t j = threadIdx.x; j < g.N; j += nb) part[j] = 0.f;
+        for (int sl = 0; sl < g.rpp; ++sl) {
+            __syncthreads();
+            if (slot == sl) {
+#pragma unroll
+                for (int k = 0; k < CPT; ++k)
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+                        if (cm.valid(k, v, g.N)) part[cm.col0[k] + v] += acc[k * V + v];
+            }
+        }
+        __syncthreads();
+        for (int64_t j = threadIdx.x; j < g.N; j += nb) out[j * cs] = part[j];
+        return;
+    }
     __syncthreads();   // previous users of `part` are done
 #pragma unroll
     for (int e = 0; e < E; ++e) part[e * nb + threadIdx.x] = acc[e];
@@ -92,7 +135,7 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, const flo
                 const int e = k * V + v;
                 float s = part[e * nb + lane];
                 for (int sl = 1; sl < g.rpp; ++sl) s += part[e * nb + sl * g.tpr + lane];
-                if (cm.valid(k, v, g.N)) out[cm.col0[k] + v] = s;
+                if (cm.valid(k, v, g.N)) out[(int64_t)(cm.col0[k] + v) * cs] = s;
             }
     }
 }
@@ -100,7 +143,7 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, const flo
 // ================================================================================== DyT
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, const PT* __restrict__ beta, T* __restrict__ y,
                Geom g) {
@@ -111,7 +154,7 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
     load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
     load_param<T, PT, MODE, CPT>(beta, g.N, c.cm, be);
     const float alpha = to_f32(alpha_p[0]);
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -137,10 +180,10 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws,
-               int64_t ng, Geom g) {
+               Geom g) {
     constexpr int V = Elems<T, MODE>::value;
     constexpr int E = CPT * V;
     extern __shared__ float part[];
@@ -153,7 +196,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
 
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -189,11 +232,13 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
             }
         }
     }
-    float* out = ws + (int64_t)blockIdx.x * ng;
-    write_partial<T, MODE, CPT>(out, acc_g, c.cm, c.slot, c.lane, g, part);
-    write_partial<T, MODE, CPT>(out + g.N, acc_b, c.cm, c.slot, c.lane, g, part);
+    // Partial row c.wg; this workgroup's column block of dgamma | dbeta, and its own dalpha
+    // column 2N + cblk (stage 2 adds the ncb dalpha columns together).
+    float* out = ws + c.wg * g.ws_rs;
+    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+    write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
     const float da = block_sum(acc_a, red);
-    if (threadIdx.x == 0) out[2 * g.N] = da;
+    if (threadIdx.x == 0) out[(2 * g.N + c.cblk) * g.ws_cs] = da;
 }
 
 // ============================================================================ LayerNorm
@@ -236,7 +281,7 @@ __device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta,
               float eps, T* __restrict__ y, float* __restrict__ mean_out,
               float* __restrict__ rstd_out, Geom g) {
@@ -248,7 +293,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
     float ga[E], be[E];
     load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
     load_param_or<T, PT, MODE, CPT>(beta, 0.f, g.N, c.cm, be);
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -280,10 +325,10 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
               const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
-              T* __restrict__ dx, float* __restrict__ ws, int64_t ng, Geom g) {
+              T* __restrict__ dx, float* __restrict__ ws, Geom g) {
     constexpr int V = Elems<T, MODE>::value;
     constexpr int E = CPT * V;
     extern __shared__ float part[];
@@ -297,7 +342,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
 
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -352,9 +397,9 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
             }
         }
     }
-    float* out = ws + (int64_t)blockIdx.x * ng;
-    write_partial<T, MODE, CPT>(out, acc_g, c.cm, c.slot, c.lane, g, part);
-    write_partial<T, MODE, CPT>(out + g.N, acc_b, c.cm, c.slot, c.lane, g, part);
+    float* out = ws + c.wg * g.ws_rs;
+    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+    write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
 }
 
 // ============================================================================== RMSNorm
@@ -382,7 +427,7 @@ __device__ __forceinline__ void rms_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps,
                T* __restrict__ y, float* __restrict__ rstd_out, Geom g) {
     constexpr int V = Elems<T, MODE>::value;
@@ -392,7 +437,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
     load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -423,10 +468,10 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT>
-__global__ void __launch_bounds__(MaxBlock<RT>::value)
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                const PT* __restrict__ weight, float eps, T* __restrict__ dx,
-               float* __restrict__ ws, int64_t ng, Geom g) {
+               float* __restrict__ ws, Geom g) {
     constexpr int V = Elems<T, MODE>::value;
     constexpr int E = CPT * V;
     extern __shared__ float part[];
@@ -439,7 +484,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_w[e] = 0.f;
 
-    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
         bool ok[RT];
         int64_t row[RT];
@@ -489,40 +534,51 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
             }
         }
     }
-    float* out = ws + (int64_t)blockIdx.x * ng;
-    write_partial<T, MODE, CPT>(out, acc_w, c.cm, c.slot, c.lane, g, part);
+    float* out = ws + c.wg * g.ws_rs;
+    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_w, c.cm, c.slot, c.lane, g, part);
 }
 
 // ============================================================================ stage 2
 
-// out columns: [0, N) -> out0, [N, 2N) -> out1, 2N -> out2[0] (NULL outputs are skipped).
-// Workgroup of `blockDim.x` threads = cb columns x G partial-row lanes; lane l adds partial
-// rows l, l + G, ... in order in float64, then the G lane sums are added as a fixed tree.
+// Stage 2.  Partial row p, column c is ws[p * rs + c * cs].  Output columns: [0, N) -> out0,
+// [N, 2N) -> out1, 2N -> out2[0] (NULL outputs are skipped).  A workgroup covers cb columns
+// with L = blockDim.x / cb lanes each; lane l adds partial rows l, l + L, ... in order in
+// float64, then the L lane sums are added as a fixed tree.  Threads are laid out along the
+// contiguous dimension of ws (columns when cs == 1, partial rows otherwise) so loads coalesce.
 template <typename PT>
 __global__ void __launch_bounds__(512)
-colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t N, int cb,
-                 PT* __restrict__ out0, PT* __restrict__ out1, PT* __restrict__ out2) {
+colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
+                 int64_t N, int cb, PT* __restrict__ out0, PT* __restrict__ out1,
+                 PT* __restrict__ out2) {
+    // Columns [2N, ng) are the dalpha partial columns of the column blocks: the lanes of column
+    // 2N add all of them (column by column, in order); the others stay idle.
     __shared__ double red[512];
-    const int G = blockDim.x / cb;
-    const int cl = threadIdx.x % cb, gl = threadIdx.x / cb;
+    const int L = blockDim.x / cb;
+    const bool col_fast = cs == 1;
+    const int cl = col_fast ? (int)(threadIdx.x % cb) : (int)(threadIdx.x / L);
+    const int gl = col_fast ? (int)(threadIdx.x / cb) : (int)(threadIdx.x % L);
     const int64_t col = (int64_t)blockIdx.x * cb + cl;
     double acc = 0.0;
-    if (col < ng) {
-        int64_t p = gl;
-        for (; p + 3 * G < P; p += 4 * G) {
-            const float a0 = ws[p * ng + col], a1 = ws[(p + G) * ng + col];
-            const float a2 = ws[(p + 2 * G) * ng + col], a3 = ws[(p + 3 * G) * ng + col];
-            acc += a0; acc += a1; acc += a2; acc += a3;
+    const int64_t c_end = col == 2 * N ? ng : col + 1;
+    if (col < ng && col <= 2 * N) {
+        for (int64_t cc = col; cc < c_end; ++cc) {
+            const float* base = ws + cc * cs;
+            int64_t p = gl;
+            for (; p + 3 * L < P; p += 4 * L) {
+                const float a0 = base[p * rs], a1 = base[(p + L) * rs];
+                const float a2 = base[(p + 2 * L) * rs], a3 = base[(p + 3 * L) * rs];
+                acc += a0; acc += a1; acc += a2; acc += a3;
+            }
+            for (; p < P; p += L) acc += base[p * rs];
         }
-        for (; p < P; p += G) acc += ws[p * ng + col];
     }
-    red[threadIdx.x] = acc;
+    red[gl * cb + cl] = acc;
     __syncthreads();
-    for (int st = G / 2; st > 0; st >>= 1) {
+    for (int st = L / 2; st > 0; st >>= 1) {
         if (gl < st) red[gl * cb + cl] += red[(gl + st) * cb + cl];
         __syncthreads();
     }
-    if (gl == 0 && col < ng) {
+    if (gl == 0 && col < ng && col <= 2 * N) {
         const PT v = from_f32<PT>((float)red[cl]);
         if (col < N) {
             if (out0) out0[col] = v;

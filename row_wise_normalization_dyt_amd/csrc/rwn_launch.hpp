@@ -1,6 +1,7 @@
 // Host-side launch plan and kernel dispatch (shared by the launcher and API translation units).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,7 +14,7 @@ namespace rwn {
 enum Layer { LAYER_DYT = 0, LAYER_LN = 1, LAYER_RMS = 2 };
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
-// Widest row a plan covers: 16 waves x 64 lanes x CPT chunks (CPT <= 2 for bf16, 4 for f32).
+// Widest row a plan covers: 16 waves x 64 lanes x 2 chunks (bf16) or x 4 chunks (f32).
 constexpr int64_t kMaxN = 16384;
 
 struct Plan {
@@ -25,9 +26,16 @@ struct Plan {
     int block = 64;           // workgroup size
     int64_t ntiles = 0;       // row tiles of rpp * rt rows
     int64_t grid = 0;         // workgroups (= partial rows of a backward)
+    int64_t kt = 1;           // blocked assignment: consecutive tiles per workgroup
+    int strided = 0;          // 1: grid-stride over tiles (grid * rpp a multiple of V)
+    int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
     int base_shift = 0;       // SHIFTED: base misalignment in elements
+    int64_t ws_rs = 0;        // backward partials: element (p, c) at ws[p * ws_rs + c * ws_cs]
+    int64_t ws_cs = 0;
     size_t lds_bytes = 0;     // dynamic LDS of the backward stage 1
     int64_t M = 0, N = 0;
+
+    int64_t partial_rows() const { return grid / ncb; }
 };
 
 // Plan for one call.  misalign_bytes: address of the [M, N] operands modulo 16 (a multiple of
@@ -35,9 +43,10 @@ struct Plan {
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misalign_bytes,
                int cus, Plan* out);
 
-// Partial-row columns of a backward: 2N+1 (DyT), 2N (LayerNorm), N (RMSNorm).
-inline int64_t partial_cols(int layer, int64_t N) {
-    return layer == LAYER_DYT ? 2 * N + 1 : layer == LAYER_LN ? 2 * N : N;
+// Partial-row columns of a backward: 2N + ncb (DyT: dgamma | dbeta | one dalpha column per
+// column block), 2N (LayerNorm), N (RMSNorm).
+inline int64_t partial_cols(int layer, int64_t N, int ncb = 1) {
+    return layer == LAYER_DYT ? 2 * N + ncb : layer == LAYER_LN ? 2 * N : N;
 }
 
 inline Geom make_geom(const Plan& p) {
@@ -45,6 +54,11 @@ inline Geom make_geom(const Plan& p) {
     g.M = p.M;
     g.N = p.N;
     g.ntiles = p.ntiles;
+    g.kt = p.kt;
+    g.ws_rs = p.ws_rs;
+    g.ws_cs = p.ws_cs;
+    g.strided = p.strided;
+    g.ncb = p.ncb;
     g.tpr = p.tpr;
     g.rpp = p.rpp;
     g.base_shift = p.base_shift;
@@ -64,28 +78,52 @@ hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
     return hipErrorInvalidValue;
 }
 
-// Calls f(IC<MODE>, IC<CPT>, IC<RT>) for the instantiated shapes.  Vector modes use CPT = 4
-// only for float32 (E = CPT * V <= 16 elements per thread per row).
+// Calls f(IC<MODE>, IC<CPT>, IC<RT>) for the instantiated shapes.
 template <typename T, typename F>
 hipError_t dispatch_shape(const Plan& p, F&& f) {
-    constexpr bool f32 = sizeof(T) == 4;
     if (p.mode == MODE_ALIGNED) {
         if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{});
+        if (p.rt == 2 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{});
         if (p.rt == 1) {
             if (p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{});
             if (p.cpt == 2) return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{});
-            if constexpr (f32) if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{});
+            if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{});
         }
     } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
         if (p.cpt == 1) return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{});
         if (p.cpt == 2) return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{});
-        if constexpr (f32) if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{});
+        if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{});
     } else if (p.mode == MODE_SCALAR && p.rt == 1) {
         if (p.cpt == 1) return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{});
         if (p.cpt == 2) return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{});
         if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{});
     }
     return hipErrorInvalidValue;
+}
+
+// Largest workgroup each kernel shape is compiled for (its amdgpu_flat_work_group_size):
+// narrow plans (RT > 1) 256 threads; one chunk per thread, and bfloat16 with four, 512;
+// otherwise 1024.  The planner keeps to it and every launcher checks it.
+constexpr int max_block(int rt, int cpt, int esz) {
+    return rt > 1 ? 256 : (cpt == 1 || (cpt == 4 && esz == 2)) ? 512 : 1024;
+}
+
+// Trace events of the next launch on this thread (set by the API while tracing).  When set,
+// the kernel goes out through hipExtLaunchKernelGGL, which records the start and stop
+// timestamps inside the dispatch packet itself instead of as separate queue packets.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <typename K, typename... Args>
+hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    const LaunchEvents ev = launch_events();
+    if (ev.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- launchers (one per kernel)
@@ -105,9 +143,10 @@ hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
 hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                           const float* rstd, const void* w, float eps, void* dx, float* ws,
                           hipStream_t s);
-// Stage 2: P partial rows of ng columns -> out0 [N], out1 [N], out2 [1] in param dtype pdt.
-hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t N,
-                            void* out0, void* out1, void* out2, hipStream_t s);
+// Stage 2: P partial rows of ng columns (element (p, c) at ws[p * rs + c * cs]) ->
+// out0 [N], out1 [N], out2 [1] in param dtype pdt.
+hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
+                            int64_t N, void* out0, void* out1, void* out2, hipStream_t s);
 hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 }  // namespace rwn

@@ -116,7 +116,7 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
     for mis in range(0, 16, esz):
         for layer in ("dyt", "layernorm", "rmsnorm"):
             V = 16 // esz
-            if (N % V or mis) and N > 16384 - (V - 1):
+            if (N % V or mis) and N > 16384 - (V - 1) and layer != "dyt":
                 # documented limit: a misaligned row of this width needs a 2049th chunk slot
                 with pytest.raises(rwn.RwnError, match="UNSUPPORTED"):
                     rwn.plan(layer, backward, M, N, dtype, misalign_bytes=mis, cus=256)
@@ -125,26 +125,43 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
             V = p["vec"]
             # chunks of a row: worst shift is V-1 elements in the shifted mode
             chunks = -(-(N + (V - 1 if p["mode"] == 1 else 0)) // V)
-            assert p["tpr"] * p["cpt"] >= chunks, p
+            assert p["tpr"] * p["cpt"] * p["ncb"] >= chunks, p
+            assert p["grid"] % p["ncb"] == 0 and (p["ncb"] == 1 or layer == "dyt")
             assert p["block"] == p["tpr"] * p["rpp"] and p["block"] <= 1024 and p["block"] % 64 == 0 or p["block"] < 64
+            # launch bounds: one chunk per thread (and bf16 with four) at most 512 threads
+            if p["rt"] == 1 and (p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2)):
+                assert p["block"] <= 512, p
             assert p["tpr"] <= 64 and (p["tpr"] & (p["tpr"] - 1)) == 0 or p["tpr"] % 64 == 0, p
             if p["mode"] == 0:
                 assert N % V == 0 and mis == 0
             if p["mode"] == 1:
-                assert p["rpp"] == 1 and p["rt"] == 1
+                assert p["rt"] == 1 and (p["rpp"] == 1 or p["rpp"] % V == 0)
             rows_per_tile = p["rpp"] * p["rt"]
             assert p["ntiles"] * rows_per_tile >= M > (p["ntiles"] - 1) * rows_per_tile
-            assert 1 <= p["grid"] <= max(p["ntiles"], 1)
-            if p["grid"] < p["ntiles"]:
-                # every thread of a shifted plan must revisit rows with the same shift
-                assert (p["grid"] * p["rpp"]) % V == 0
+            if p["strided"]:
+                gt = p["grid"] // p["ncb"]              # tile stride
+                assert 1 <= gt <= max(p["ntiles"], 1)
+                if gt < p["ntiles"]:
+                    # a thread revisits rows gt * rpp apart: they must share the shift
+                    assert (gt * p["rpp"]) % V == 0
+            else:
+                # blocked: consecutive tiles, every tile covered exactly once
+                assert p["grid"] * p["kt"] >= p["ntiles"] > (p["grid"] - 1) * p["kt"]
+                if p["mode"] == 1 and p["rpp"] > 1:
+                    assert p["rpp"] % V == 0, p    # slot s always sees rows = s mod V
+                if not backward:
+                    assert p["kt"] == 1
 
 
 def test_plan_uses_narrow_tiles_for_narrow_rows():
     p = rwn.plan("layernorm", True, 401408, 24, torch.float32, cus=256)
-    assert p["mode"] == 0 and p["tpr"] == 8 and p["rpp"] == 32 and p["rt"] == 4
+    assert p["mode"] == 0 and p["tpr"] == 8 and p["rpp"] == 32
     p = rwn.plan("dyt", True, 1048573, 32, torch.bfloat16, cus=256)
     assert p["tpr"] == 4 and p["rpp"] == 64
+    # grid-stride plans keep at least 8 waves per CU resident
+    for bwd in (False, True):
+        p = rwn.plan("layernorm", bwd, 401408, 24, torch.float32, cus=256)
+        assert p["strided"] and p["grid"] * p["block"] // 64 >= 8 * 256 and p["grid"] % 8 == 0
     # short input: the tile count caps the grid (no full grid for one row)
     p = rwn.plan("rmsnorm", False, 1, 128, torch.bfloat16, cus=256)
     assert p["grid"] == 1 and p["ntiles"] == 1
@@ -154,3 +171,37 @@ def test_plan_is_deterministic():
     a = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
     b = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
     assert a == b
+
+
+_BOUNDS_SCRIPT = r"""
+import sys, torch
+sys.path.insert(0, {root!r})
+import row_wise_normalization_dyt_amd as rwn
+bad = []
+for layer in ("dyt", "layernorm", "rmsnorm"):
+    for dt, esz in ((torch.float32, 4), (torch.bfloat16, 2)):
+        for N in (24, 64, 129, 1025, 2048, 4096, 8192, 16384):
+            for mis in range(0, 16, esz):
+                for bwd in (0, 1):
+                    try:
+                        p = rwn.plan(layer, bwd, 65537, N, dt, mis, cus=256)
+                    except rwn.RwnError:
+                        continue
+                    cap = 256 if p["rt"] > 1 else (512 if p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2) else 1024)
+                    if p["block"] > cap or p["block"] != p["tpr"] * p["rpp"]:
+                        bad.append((layer, str(dt), N, mis, bwd, p))
+print("BAD", bad)
+"""
+
+
+@pytest.mark.parametrize("env", ["RWN_WIDE_BLOCK=1024", "RWN_WIDE_BLOCK=64", "RWN_FWD_RT=4", "RWN_BWD_RT=2",
+                                 "RWN_MIN_WAVES=32", "RWN_WINDOW_KB=64", "RWN_BLOCKED_K=3"])
+def test_plans_respect_kernel_launch_bounds_under_tuning_overrides(env):
+    """Every plan's workgroup fits the launch bound its kernel was compiled for, also with the
+    tuning overrides set (a plan over the bound would fail to launch)."""
+    import subprocess, sys
+    k, v = env.split("=")
+    r = subprocess.run([sys.executable, "-c", _BOUNDS_SCRIPT.format(root=os.path.dirname(os.path.dirname(__file__)))],
+                       env=dict(os.environ, **{k: v}), capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "BAD []" in r.stdout, r.stdout[-2000:]
