@@ -25,6 +25,7 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
+//   RWN_XCD_REMAP           0: keep hardware workgroup numbering (default 1: XCD-contiguous)
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -40,6 +41,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
     static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
     static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
+    static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -153,6 +155,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         }
         p.grid = gt * p.ncb;
         p.kt = 0;
+        p.xcd_remap = (xcd_remap && p.grid % 8 == 0) ? 1 : 0;
     }
     if (backward) {
         // Partials column-major when rows are short (stage 2 then reads each column

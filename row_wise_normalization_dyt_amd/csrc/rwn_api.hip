@@ -463,5 +463,6 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
     out[9] = p.strided ? 0 : p.kt;
     out[10] = p.strided;
     out[11] = p.ncb;
+    out[12] = p.xcd_remap;
     return ok();
 }

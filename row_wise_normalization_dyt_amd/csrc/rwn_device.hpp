@@ -50,6 +50,7 @@ struct Geom {
     int strided;      // 1: workgroup w visits tiles w, w + grid, ...; 0: tiles [w*kt, (w+1)*kt)
     int ncb;          // column blocks per row (DyT only; 1 otherwise): workgroup w keeps
                       // column block w % ncb and strides over tiles by grid / ncb
+    int xcd_remap;    // 1: renumber workgroups so consecutive numbers share an XCD (grid % 8 == 0)
     float inv_n;      // 1 / N
 };
 
@@ -147,14 +148,19 @@ __device__ __forceinline__ uint32_t raw_bits(const T* p) {
     else return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
 }
 
-// Load the CPT chunks of row `row` of p (row pitch N); columns outside the row read as 0, and
-// `rowvalid` false reads nothing (all zeros).
+// Load the CPT chunks of row `row` of p (row pitch N, `total` = M * N elements); columns
+// outside the row read as 0, and `rowvalid` false reads nothing (all zeros).  A chunk cut by
+// the row's ends still lies inside the matrix (its other elements belong to the neighbouring
+// row), so it is read with one 16-byte load and the foreign elements are zeroed; only a chunk
+// that would reach outside [0, total) -- the first row's head or the last row's tail -- is
+// read element by element.
 template <typename T, int MODE, int CPT>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, int64_t row, int64_t N,
-                                         const ColMap<T, MODE, CPT>& cm, bool rowvalid,
-                                         RowRegs<T, MODE, CPT>& r) {
+                                         int64_t total, const ColMap<T, MODE, CPT>& cm,
+                                         bool rowvalid, RowRegs<T, MODE, CPT>& r) {
     constexpr int V = RowRegs<T, MODE, CPT>::V;
     constexpr int W = RowRegs<T, MODE, CPT>::W;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const T* rp = p + row * N;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -164,17 +170,31 @@ __device__ __forceinline__ void load_row(const T* __restrict__ p, int64_t row, i
         if (MODE == MODE_SCALAR) {
             r.w[k][0] = raw_bits(rp + cm.col0[k]);
         } else if (MODE == MODE_ALIGNED || cm.full[k]) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
             const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + cm.col0[k]));
             r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
         } else {
+            const int64_t g0 = row * N + cm.col0[k];
+            if (g0 >= 0 && g0 + V <= total) {
+                u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + cm.col0[k]));
+                // zero the elements of the neighbouring rows
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int j = cm.col0[k] + v;
-                if (j >= 0 && (int64_t)j < N) {
-                    const uint32_t b = raw_bits(rp + j);
-                    if constexpr (sizeof(T) == 4) r.w[k][v] = b;
-                    else r.w[k][v >> 1] |= b << (16 * (v & 1));
+                for (int e = 0; e < V; ++e) {
+                    const int j = cm.col0[k] + e;
+                    if (j < 0 || (int64_t)j >= N) {
+                        if constexpr (sizeof(T) == 4) v[e] = 0u;
+                        else v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                    }
+                }
+                r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int j = cm.col0[k] + v;
+                    if (j >= 0 && (int64_t)j < N) {
+                        const uint32_t b = raw_bits(rp + j);
+                        if constexpr (sizeof(T) == 4) r.w[k][v] = b;
+                        else r.w[k][v >> 1] |= b << (16 * (v & 1));
+                    }
                 }
             }
         }

@@ -46,8 +46,13 @@ struct RowCtx {
     __device__ __forceinline__ RowCtx(const Geom& g) {
         slot = threadIdx.x / g.tpr;
         lane = threadIdx.x - slot * g.tpr;
-        cblk = (int)(blockIdx.x % g.ncb);
-        wg = blockIdx.x / g.ncb;
+        // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  The
+        // remap gives consecutive logical numbers -- and so neighbouring rows, whose shared
+        // cache lines both write -- to workgroups on the same XCD.
+        int64_t b = blockIdx.x;
+        if (g.xcd_remap) b = (b % 8) * (gridDim.x / 8) + b / 8;
+        cblk = (int)(b % g.ncb);
+        wg = b / g.ncb;
         rows_per_tile = (int64_t)g.rpp * RT;
         if (g.strided) {
             t_begin = wg;
@@ -162,7 +167,7 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
         }
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -204,8 +209,8 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
         }
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -301,7 +306,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
         }
         float mu[RT], rs[RT];
         ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
@@ -351,8 +356,8 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
             if (have_stats) {
                 mu[u] = ok[u] ? mean_in[row[u]] : 0.f;
                 rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
@@ -445,7 +450,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
         }
         float rs[RT];
         rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
@@ -493,8 +498,8 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
         for (int u = 0; u < RT; ++u) {
             row[u] = c.row(tile, u, g);
             ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, c.cm, ok[u], gr[u]);
+            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
+            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
             if (rstd_in) rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
         }
         if (!rstd_in) rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);

@@ -29,6 +29,7 @@ struct Plan {
     int64_t kt = 1;           // blocked assignment: consecutive tiles per workgroup
     int strided = 0;          // 1: grid-stride over tiles (grid * rpp a multiple of V)
     int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
+    int xcd_remap = 0;        // renumber workgroups XCD-contiguously (needs grid % 8 == 0)
     int base_shift = 0;       // SHIFTED: base misalignment in elements
     int64_t ws_rs = 0;        // backward partials: element (p, c) at ws[p * ws_rs + c * ws_cs]
     int64_t ws_cs = 0;
@@ -59,6 +60,7 @@ inline Geom make_geom(const Plan& p) {
     g.ws_cs = p.ws_cs;
     g.strided = p.strided;
     g.ncb = p.ncb;
+    g.xcd_remap = p.xcd_remap;
     g.tpr = p.tpr;
     g.rpp = p.rpp;
     g.base_shift = p.base_shift;

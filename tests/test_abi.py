@@ -127,6 +127,8 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
             chunks = -(-(N + (V - 1 if p["mode"] == 1 else 0)) // V)
             assert p["tpr"] * p["cpt"] * p["ncb"] >= chunks, p
             assert p["grid"] % p["ncb"] == 0 and (p["ncb"] == 1 or layer == "dyt")
+            if p["xcd_remap"]:
+                assert p["grid"] % 8 == 0      # the renumbering is a bijection
             assert p["block"] == p["tpr"] * p["rpp"] and p["block"] <= 1024 and p["block"] % 64 == 0 or p["block"] < 64
             # launch bounds: one chunk per thread (and bf16 with four) at most 512 threads
             if p["rt"] == 1 and (p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2)):
