@@ -157,13 +157,15 @@ int rwn_trace_end(float* ms, int* tags, int capacity);
 rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Launch plan the library chooses for an entry point (introspection for tests and tuning).
- * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 13 integers to out:
+ * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 14 integers to out:
  * {mode (0 aligned vectors, 1 shifted vectors, 2 scalar), chunks per thread, rows per thread,
  *  threads per row, row slots per workgroup, workgroup size, workgroups, row tiles,
  *  elements per chunk, row tiles per workgroup (0 when strided), strided (1: workgroup w
  *  visits tiles w, w + workgroups / column blocks, ...), column blocks per row, XCD remap
- *  (1: workgroup numbers renumbered so consecutive ones share an XCD)}.  misalign_bytes is the common address of x/y/dy/dx modulo 16; cus is
- * the compute-unit count to plan for (0: query the current device). */
+ *  (1: workgroup numbers renumbered so consecutive ones share an XCD), prefetch (1: the next
+ *  tile's loads are issued before the current tile is processed)}.  misalign_bytes is the
+ * common address of x/y/dy/dx modulo 16; cus is the compute-unit count to plan for (0: query
+ * the current device). */
 rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
                     int misalign_bytes, int cus, int64_t* out);
 

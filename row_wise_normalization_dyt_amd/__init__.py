@@ -272,8 +272,9 @@ def plan(layer: str, backward: bool, M: int, N: int, dtype: torch.dtype, misalig
     """The launch plan the library picks.  cus = 0 plans for the current device; any other value
     plans for that many compute units without touching a device."""
     lib = _L()
-    out = (ctypes.c_int64 * 13)()
+    out = (ctypes.c_int64 * 14)()
     li = {"dyt": 0, "layernorm": 1, "rmsnorm": 2}[layer]
     _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], misalign_bytes, cus, out))
-    keys = ("mode", "cpt", "rt", "tpr", "rpp", "block", "grid", "ntiles", "vec", "kt", "strided", "ncb", "xcd_remap")
+    keys = ("mode", "cpt", "rt", "tpr", "rpp", "block", "grid", "ntiles", "vec", "kt", "strided", "ncb", "xcd_remap",
+            "prefetch")
     return dict(zip(keys, [int(v) for v in out]))

@@ -1,6 +1,9 @@
 // Launch planning, the stage-2 column reduction and the copy probe.
 #include <stdlib.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -20,12 +23,13 @@ static int64_t next_pow2(int64_t v) {
 // Tuning overrides, read once (each changes the launch plan, and with it the reduction order
 // and so the low bits of parameter gradients):
 //   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4)
-//   RWN_WINDOW_KB           target bytes of one tensor touched per grid-stride step
+//   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
 //   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
 //   RWN_XCD_REMAP           0: keep hardware workgroup numbering (default 1: XCD-contiguous)
+//   RWN_PREFETCH            0 / 1: force the plain / pipelined tile loop where both exist
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -37,11 +41,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
                int cus, Plan* out) {
     static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
     static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 1);
-    static const int window_kb = env_int("RWN_WINDOW_KB", 64, 1 << 20, 2048);
+    static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
     static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
     static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
     static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, 1);
+    static const int prefetch = env_int("RWN_PREFETCH", 0, 1, -1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -123,6 +128,16 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         p.rpp = p.tpr >= target ? 1 : target / p.tpr;
     }
     if (p.ncb > 1 && p.mode == MODE_SHIFTED) p.rpp = 1;
+    // Pipelined tile loop (measured): it pays in forwards with one chunk per thread (except
+    // the SHIFTED LayerNorm / RMSNorm ones) and in 16-wave rows, and in SHIFTED backwards;
+    // elsewhere the doubled input registers cost more than the overlap gains.  Shapes with
+    // more than two chunks per thread have no pipelined form.
+    if (p.cpt * p.rt <= 2) {
+        const bool one = p.cpt * p.rt == 1;
+        if (prefetch >= 0) p.pf = prefetch;
+        else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
+        else p.pf = (p.mode == MODE_SHIFTED && one) ? 1 : 0;
+    }
     // Keep to the kernel shape's launch bound (tpr itself always fits: see the wave limits).
     const int maxb = max_block(p.rt, p.cpt, esz);
     if (p.tpr * p.rpp > maxb) p.rpp = maxb / p.tpr > 0 ? maxb / p.tpr : 1;
@@ -136,22 +151,34 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         p.kt = blocked_k;
         p.grid = (p.ntiles + p.kt - 1) / p.kt;
     } else {
-        // Persistent grid-stride.  HBM streams best when the bytes in flight come from a
-        // compact address window: size the grid so one stride step covers ~window_kb of each
-        // tensor, but never below min_waves resident waves per CU.  With ncb column blocks the
-        // grid is ncb workgroups per tile stride.
+        // Persistent grid-stride with c workgroups per CU, all resident at once.  c spans
+        // [16, 28] resident waves per CU (fewer waves leave HBM latency exposed; more add
+        // nothing).  Within that range the c whose tile count per workgroup is most even wins:
+        // the kernel lasts as long as its busiest workgroup, so ntiles / gt against
+        // ceil(ntiles / gt) is the fraction of the machine kept busy to the end.  Ties go to
+        // fewer waves.  With ncb column blocks the grid is ncb workgroups per tile stride.
         p.strided = 1;
-        const double tile_bytes = (double)rows_per_tile * (double)N * esz;
-        int64_t gt = (int64_t)((double)window_kb * 1024.0 / tile_bytes);
         const int64_t waves_per_wg = (p.block + 63) / 64;
-        const int64_t gmin = ((int64_t)cus * min_waves + waves_per_wg * p.ncb - 1) / (waves_per_wg * p.ncb);
-        if (gt < gmin) gt = gmin;
-        if (gt * p.ncb > (int64_t)cus * 32) gt = (int64_t)cus * 32 / p.ncb;
-        if (gt >= p.ntiles) {
-            gt = p.ntiles;                     // one tile per workgroup
-        } else {
-            gt -= gt % 8;                      // SHIFTED: the tile stride * rpp must be a multiple of V
+        const int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
+        const int64_t c_lo = std::min(c_max, std::max<int64_t>(1, (min_waves + waves_per_wg - 1) / waves_per_wg));
+        const int64_t c_hi = std::max<int64_t>(c_lo, 28 / waves_per_wg);
+        int64_t gt = 0;
+        double best = -1.0;
+        for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+            if (wg_per_cu > 0 && cc != wg_per_cu) continue;
+            int64_t cand = (int64_t)cus * cc / p.ncb;
+            cand -= cand % 8;                  // SHIFTED: the tile stride * rpp must be a multiple of V
+            if (cand < 8) cand = 8;
+            if (cand >= p.ntiles) { gt = p.ntiles; break; }   // one tile per workgroup
+            const double per = (double)p.ntiles / (double)cand;
+            const double eff = per / std::ceil(per) - 0.005 * (double)(cc - c_lo);
+            if (eff > best + 1e-9) { best = eff; gt = cand; }
+        }
+        if (gt == 0) {   // forced c out of range: nearest in-range candidate
+            gt = (int64_t)cus * (wg_per_cu > 0 ? std::min<int64_t>(wg_per_cu, c_max) : c_lo) / p.ncb;
+            gt -= gt % 8;
             if (gt < 8) gt = 8;
+            if (gt > p.ntiles) gt = p.ntiles;
         }
         p.grid = gt * p.ncb;
         p.kt = 0;

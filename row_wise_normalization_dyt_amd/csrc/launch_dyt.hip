@@ -1,4 +1,6 @@
-// DyT launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT).
+// DyT launchers: forward and backward stage 1 for every (dtype pair, mode, RT, prefetch).  DyT plans
+// always take one chunk per thread (wide rows are cut into column blocks instead), so the
+// CPT > 1 shapes are not instantiated.
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -10,11 +12,12 @@ hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
-            if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
-            return launch(dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>,
+            if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
+            else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+            else return launch(dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)alpha, (const PT*)gamma, (const PT*)beta, (T*)y, g);
         });
@@ -28,11 +31,12 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
-            if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
-            return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>,
+            if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
+            else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+            else return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                               decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                                (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, g);
         });

@@ -1,4 +1,4 @@
-// LayerNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT).
+// LayerNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT, prefetch).
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -11,11 +11,11 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             return launch(ln_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                              decltype(rt)::value>,
+                                              decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)gamma, (const PT*)beta, eps, (T*)y, mean, rstd, g);
         });
@@ -29,11 +29,11 @@ hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const v
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             return launch(ln_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                              decltype(rt)::value>,
+                                              decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                                (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
         });

@@ -1,4 +1,4 @@
-// RMSNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT).
+// RMSNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT, prefetch).
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -10,11 +10,11 @@ hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             return launch(rms_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>,
+                                               decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)w, eps, (T*)y, rstd, g);
         });
@@ -28,11 +28,11 @@ hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             return launch(rms_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value>,
+                                               decltype(rt)::value, decltype(pf)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                                (const T*)dy, rstd, (const PT*)w, eps, (T*)dx, ws, g);
         });

@@ -69,30 +69,6 @@ template <typename T> __device__ __forceinline__ float round_through(float v) {
     return to_f32(from_f32<T>(v));
 }
 
-// ------------------------------------------------------------------------- chunk I/O
-
-template <typename T, int V> struct ChunkIO;
-
-// Activations are streamed once per kernel, so whole-chunk loads and stores carry the
-// nontemporal hint (they bypass cache retention; measured ~5-8% faster on streaming copies).
-template <> struct ChunkIO<float, 4> {
-    __device__ __forceinline__ static void store(float* p, const float* o) {
-        f32x4 v = {o[0], o[1], o[2], o[3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-    }
-};
-
-template <> struct ChunkIO<bf16_t, 8> {
-    __device__ __forceinline__ static void store(bf16_t* p, const float* o) {
-        f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-        __builtin_nontemporal_store(__builtin_convertvector(f, bf16x8), reinterpret_cast<bf16x8*>(p));
-    }
-};
-
-template <typename T> struct ChunkIO<T, 1> {
-    __device__ __forceinline__ static void store(T* p, const float* o) { *p = from_f32<T>(o[0]); }
-};
-
 // Per-thread column map: which columns each of the CPT chunks covers (fixed for all rows the
 // thread visits) and whether the chunk is whole inside the row.
 template <typename T, int MODE, int CPT>
@@ -142,41 +118,100 @@ struct RowRegs {
     }
 };
 
-template <typename T>
-__device__ __forceinline__ uint32_t raw_bits(const T* p) {
-    if constexpr (sizeof(T) == 4) return *reinterpret_cast<const uint32_t*>(p);
-    else return (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+// ------------------------------------------------------------------ buffer loads
+// Row loads go through buffer descriptors rather than flat pointers.  A buffer load whose
+// offset lies past the descriptor's record count returns zeros without touching memory, so a
+// padded row or column needs no branch around its load: its offset is simply pushed out of
+// range.  Branch-free loads are what let the compiler keep the next tile's loads in flight
+// while the current one is used (a load under a branch forces a full wait after it).
+//
+// One descriptor covers one row tile of one tensor: its base is the tile's first element
+// (SHIFTED: the 16-byte block holding it), its record count the bytes from there to the
+// tensor's end (rounded up to 16: the aligned block that holds the last element), capped at
+// 1 GiB -- a tile spans at most 16 rows of 16384 float32, far less.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above every record count
+constexpr int64_t kMaxRecords = int64_t(1) << 30;
+constexpr int kBufferFormat = 0x00020000;       // descriptor word 3: 32-bit data format
+constexpr int kNontemporal = 2;                 // cache policy: streaming (nt)
+
+// The descriptor's inputs are wave-uniform by construction (they depend only on the tile);
+// reading them through readfirstlane states that to the compiler, which otherwise may not
+// prove it and would wrap every load in a loop over the distinct descriptors of the wave.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// Load the CPT chunks of row `row` of p (row pitch N, `total` = M * N elements); columns
-// outside the row read as 0, and `rowvalid` false reads nothing (all zeros).  A chunk cut by
-// the row's ends still lies inside the matrix (its other elements belong to the neighbouring
-// row), so it is read with one 16-byte load and the foreign elements are zeroed; only a chunk
-// that would reach outside [0, total) -- the first row's head or the last row's tail -- is
-// read element by element.
+// A buffer offset chosen per lane (in range or kOutOfRange), made opaque so the compiler emits
+// it as a select instead of splitting the access into a branch per case.
+__device__ __forceinline__ uint32_t lane_offset(bool in, uint32_t off) {
+    uint32_t o = in ? off : kOutOfRange;
+    asm volatile("" : "+v"(o));
+    return o;
+}
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+    bytes = bytes < 0 ? 0 : bytes > kMaxRecords ? kMaxRecords : bytes;
+    const uint64_t b = uniform_u64(reinterpret_cast<uint64_t>(base));
+    const int n = (int)__builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0, n, kBufferFormat);
+}
+
+// Source of one tensor's row tile; e0 is the element index (relative to the tensor) at the
+// descriptor's base.  `live` false makes every load of the tile read zeros.
+struct TileSrc {
+    Rsrc rsrc;
+    int64_t e0;
+};
+
+template <typename T, int MODE>
+__device__ __forceinline__ TileSrc tile_src(const T* __restrict__ p, int64_t row0, int64_t M, int64_t N,
+                                            int base_shift, bool live) {
+    constexpr int V = Elems<T, MODE>::value;
+    int64_t e0 = row0 * N;
+    if (MODE == MODE_SHIFTED) e0 -= (e0 + base_shift) % V;
+    int64_t bytes = (M * N - e0) * (int64_t)sizeof(T);
+    bytes = (bytes + 15) & ~int64_t(15);
+    TileSrc t;
+    t.rsrc = make_rsrc(reinterpret_cast<const char*>(p) + e0 * (int64_t)sizeof(T), live ? bytes : 0);
+    t.e0 = e0;
+    return t;
+}
+
+// One float32 per row (LayerNorm / RMSNorm statistics) of the tile starting at row0.
+__device__ __forceinline__ Rsrc stats_src(const float* p, int64_t row0, int64_t M, bool live) {
+    return p ? make_rsrc(p + row0, live ? (M - row0) * 4 : 0) : make_rsrc(nullptr, 0);
+}
+
+__device__ __forceinline__ float load_stat(Rsrc r, int64_t row, int64_t row0, bool ok) {
+    const uint32_t off = lane_offset(ok, (uint32_t)((row - row0) * 4));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Load the CPT chunks of row `row` (row pitch N) from the tile source; columns outside the row
+// read as 0, and `rowvalid` false reads zeros.  Every chunk is one 16-byte load (SCALAR: one
+// element).  A SHIFTED chunk cut by the row's ends holds elements of the neighbouring row (or,
+// at the tensor's ends, bytes of the 16-byte block beyond it), which are zeroed after the load.
 template <typename T, int MODE, int CPT>
-__device__ __forceinline__ void load_row(const T* __restrict__ p, int64_t row, int64_t N,
-                                         int64_t total, const ColMap<T, MODE, CPT>& cm,
-                                         bool rowvalid, RowRegs<T, MODE, CPT>& r) {
+__device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_t N,
+                                         const ColMap<T, MODE, CPT>& cm, bool rowvalid,
+                                         RowRegs<T, MODE, CPT>& r) {
     constexpr int V = RowRegs<T, MODE, CPT>::V;
-    constexpr int W = RowRegs<T, MODE, CPT>::W;
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const T* rp = p + row * N;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-#pragma unroll
-        for (int i = 0; i < W; ++i) r.w[k][i] = 0u;
-        if (!rowvalid || !cm.any[k]) continue;
+        const bool in = rowvalid && cm.any[k];
+        const uint32_t off = lane_offset(in, (uint32_t)((row * N + cm.col0[k] - src.e0) * (int64_t)sizeof(T)));
         if (MODE == MODE_SCALAR) {
-            r.w[k][0] = raw_bits(rp + cm.col0[k]);
-        } else if (MODE == MODE_ALIGNED || cm.full[k]) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + cm.col0[k]));
-            r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
+            if constexpr (sizeof(T) == 4)
+                r.w[k][0] = __builtin_amdgcn_raw_buffer_load_b32(src.rsrc, off, 0, 0);
+            else
+                r.w[k][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(src.rsrc, off, 0, 0);
         } else {
-            const int64_t g0 = row * N + cm.col0[k];
-            if (g0 >= 0 && g0 + V <= total) {
-                u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + cm.col0[k]));
-                // zero the elements of the neighbouring rows
+            u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src.rsrc, off, 0, kNontemporal);
+            if (MODE == MODE_SHIFTED) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
                     const int j = cm.col0[k] + e;
@@ -185,36 +220,37 @@ __device__ __forceinline__ void load_row(const T* __restrict__ p, int64_t row, i
                         else v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
                     }
                 }
-                r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
-            } else {
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const int j = cm.col0[k] + v;
-                    if (j >= 0 && (int64_t)j < N) {
-                        const uint32_t b = raw_bits(rp + j);
-                        if constexpr (sizeof(T) == 4) r.w[k][v] = b;
-                        else r.w[k][v >> 1] |= b << (16 * (v & 1));
-                    }
-                }
             }
+            r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
         }
     }
 }
 
-// Store chunk k of row `row` from V float32 values (rounded to T); only columns inside the row.
+// Store chunk k of row `row` of p (row pitch N) from V float32 values rounded to T; only
+// columns inside the row are written, nothing when `rowvalid` is false.  A whole chunk is one
+// nontemporal 16-byte store; a SHIFTED chunk cut by the row's ends is written element by element.
 template <typename T, int MODE, int CPT>
 __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int64_t N,
-                                            const ColMap<T, MODE, CPT>& cm, int k, const float* o) {
+                                            const ColMap<T, MODE, CPT>& cm, int k, const float* o,
+                                            bool rowvalid) {
     constexpr int V = ColMap<T, MODE, CPT>::V;
-    if (!cm.any[k]) return;
-    T* rp = p + row * N;
-    if (MODE != MODE_SHIFTED || cm.full[k]) {
-        ChunkIO<T, V>::store(rp + cm.col0[k], o);
+    if (!rowvalid || !cm.any[k]) return;
+    T* rp = p + row * N + cm.col0[k];
+    if constexpr (MODE == MODE_SCALAR) {
+        *rp = from_f32<T>(o[0]);
+    } else if (MODE == MODE_ALIGNED || cm.full[k]) {
+        if constexpr (sizeof(T) == 4) {
+            f32x4 v = {o[0], o[1], o[2], o[3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(rp));
+        } else {
+            f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+            __builtin_nontemporal_store(__builtin_convertvector(f, bf16x8), reinterpret_cast<bf16x8*>(rp));
+        }
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             const int j = cm.col0[k] + v;
-            if (j >= 0 && (int64_t)j < N) rp[j] = from_f32<T>(o[v]);
+            if (j >= 0 && (int64_t)j < N) rp[v] = from_f32<T>(o[v]);
         }
     }
 }
@@ -269,19 +305,22 @@ __device__ __forceinline__ float group_sum(float v, int g) {
     return v;
 }
 
+// Most waves a workgroup has (1024 threads).
+constexpr int kMaxWaves = 16;
+
 // Row sums for K values per thread.  Rows of up to 64 threads reduce inside their wave; rows
 // spanning W = tpr/64 waves add the W wave sums from LDS in wave order.  `red` holds
-// 2 * (block/64) * K floats; `parity` alternates between two halves so one barrier per
-// reduction is enough.
+// 2 * kMaxWaves * K floats; `parity` alternates between the two halves so one barrier per
+// reduction is enough.  (The halves are sized by the bound rather than by blockDim, whose
+// read is a memory load that would make the wave wait for all of its loads in flight.)
 template <int K>
 __device__ __forceinline__ void row_sum(float (&v)[K], int tpr, float* red, int& parity) {
     const int g = tpr < 64 ? tpr : 64;
 #pragma unroll
     for (int i = 0; i < K; ++i) v[i] = group_sum(v[i], g);
     if (tpr > 64) {
-        const int nw = blockDim.x >> 6;
         const int wave = threadIdx.x >> 6;
-        float* buf = red + parity * nw * K;
+        float* buf = red + parity * kMaxWaves * K;
         if ((threadIdx.x & 63) == 0) {
 #pragma unroll
             for (int i = 0; i < K; ++i) buf[wave * K + i] = v[i];

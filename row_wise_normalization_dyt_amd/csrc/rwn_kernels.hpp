@@ -11,7 +11,7 @@
 // Backward stage 1 accumulates the parameter-gradient terms of its columns in float32
 // registers over every row the thread visits, then writes one partial row per workgroup to
 // the workspace [grid, ng] (ng = 2N+1 DyT: dgamma | dbeta | dalpha; 2N LayerNorm:
-// dgamma | dbeta; N RMSNorm: dweight).  Row slots of a workgroup are combined in slot order
+// dgamma | dbeta; N RMSNorm: dweight).  Row slots of a workgroup are combined by a fixed tree
 // through LDS.  Stage 2 sums the partial rows per column in a fixed order in float64.  No
 // atomics anywhere: the reduction order depends only on the launch plan.
 #pragma once
@@ -20,7 +20,7 @@
 
 namespace rwn {
 
-constexpr int kMaxBlock = 1024;
+constexpr int kMaxBlock = 64 * kMaxWaves;
 // Largest workgroup a plan gives each kernel shape (the planner keeps to it): narrow plans
 // (RT > 1) run 256 threads; one chunk per thread, and bf16 with four, at most 8 waves per row
 // (a 256-register budget); otherwise up to 16 waves (128 registers).
@@ -30,7 +30,7 @@ template <typename T, int RT, int CPT> struct MaxBlock {
 static_assert(MaxBlock<bf16_t, 1, 4>::value == 512 && MaxBlock<float, 1, 4>::value == 1024 &&
                   MaxBlock<float, 4, 1>::value == 256 && MaxBlock<bf16_t, 1, 2>::value == 1024,
               "kernel launch bounds must match the planner's max_block()");
-constexpr int kRedFloats = 2 * (kMaxBlock / 64) * 8;   // row_sum buffers: 2 halves x waves x K<=8
+constexpr int kRedFloats = 2 * kMaxWaves * 8;   // row_sum buffers: 2 halves x waves x K <= 8
 
 // Per-thread setup common to all row kernels: slot/lane, the workgroup's tile range and the
 // thread's column map.
@@ -76,7 +76,48 @@ struct RowCtx {
     __device__ __forceinline__ int64_t row(int64_t tile, int u, const Geom& g) const {
         return tile * rows_per_tile + (int64_t)u * g.rpp + slot;
     }
+    // Rows of `tile` for this thread; a row is live when the tile is one of this workgroup's
+    // and the row exists.
+    __device__ __forceinline__ void tile_rows(int64_t tile, const Geom& g, int64_t (&r)[RT],
+                                              bool (&ok)[RT]) const {
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            r[u] = row(tile, u, g);
+            ok[u] = tile < t_end && r[u] < g.M;
+        }
+    }
 };
+
+// Software pipelining of the tile loop (kernel parameter PF, chosen by the planner).  With PF
+// the loads of the next tile are issued before the current tile is reduced, computed and
+// stored, so every wave keeps two tiles of loads in flight and the store of one tile overlaps
+// the load of the next; the registers holding a tile's inputs are doubled.  Only shapes with
+// at most two 16-byte chunks per thread per tensor have the pipelined form.
+
+// Runs body(in) for every tile of the workgroup in order; fetch(tile, in) issues the tile's
+// loads (a tile past the workgroup's range loads nothing).  The pipelined form alternates two
+// buffers instead of copying the next tile into the current one: a register copy would have
+// to wait for the loads it copies and so end the overlap.
+template <bool PF, typename In, typename Ctx, typename Fetch, typename Body>
+__device__ __forceinline__ void tile_loop(const Ctx& c, Fetch&& fetch, Body&& body) {
+    if constexpr (PF) {
+        In a, b;
+        fetch(c.t_begin, a);
+        for (int64_t tile = c.t_begin; tile < c.t_end; tile += 2 * c.t_step) {
+            fetch(tile + c.t_step, b);
+            body(a);
+            if (tile + c.t_step >= c.t_end) break;
+            fetch(tile + 2 * c.t_step, a);
+            body(b);
+        }
+    } else {
+        for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+            In cur;
+            fetch(tile, cur);
+            body(cur);
+        }
+    }
+}
 
 // Load a per-column parameter (or `dflt` for every column when p is NULL).
 template <typename T, typename PT, int MODE, int CPT>
@@ -91,7 +132,8 @@ __device__ __forceinline__ void load_param_or(const PT* __restrict__ p, float df
     }
 }
 
-// Write one gradient's partial row: out[col * cs] = sum over row slots (slot order) of acc.
+// Write one gradient's partial row: out[col * cs] = sum over the row slots of acc (a fixed
+// order that depends only on the plan).
 // `part` is LDS of max(E * blockDim.x, N) floats (only used when rpp > 1).
 template <typename T, int MODE, int CPT>
 __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t cs, const float* acc,
@@ -128,26 +170,33 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t c
         for (int64_t j = threadIdx.x; j < g.N; j += nb) out[j * cs] = part[j];
         return;
     }
+    // Slots share one column map: a fixed binary tree over the slots, every thread taking part
+    // (slot s adds slot s + st for st = P/2, P/4, ..., 1, P the power of two >= rpp).
     __syncthreads();   // previous users of `part` are done
 #pragma unroll
     for (int e = 0; e < E; ++e) part[e * nb + threadIdx.x] = acc[e];
+    int st = 1;
+    while (st < g.rpp) st <<= 1;
+    for (st >>= 1; st >= 1; st >>= 1) {
+        __syncthreads();
+        if (slot < st && slot + st < g.rpp) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) part[e * nb + threadIdx.x] += part[e * nb + threadIdx.x + st * g.tpr];
+        }
+    }
     __syncthreads();
     if (slot == 0) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k)
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int e = k * V + v;
-                float s = part[e * nb + lane];
-                for (int sl = 1; sl < g.rpp; ++sl) s += part[e * nb + sl * g.tpr + lane];
-                if (cm.valid(k, v, g.N)) out[(int64_t)(cm.col0[k] + v) * cs] = s;
-            }
+            for (int v = 0; v < V; ++v)
+                if (cm.valid(k, v, g.N)) out[(int64_t)(cm.col0[k] + v) * cs] = part[(k * V + v) * nb + lane];
     }
 }
 
 // ================================================================================== DyT
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, const PT* __restrict__ beta, T* __restrict__ y,
@@ -159,32 +208,37 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
     load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
     load_param<T, PT, MODE, CPT>(beta, g.N, c.cm, be);
     const float alpha = to_f32(alpha_p[0]);
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+    };
+    auto body = [&](const In& in) {
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < RT; ++u) {
-            if (!ok[u]) continue;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 float o[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * xr[u].get(k, v)), be[k * V + v]);
-                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+                    o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * in.xr[u].get(k, v)), be[k * V + v]);
+                store_chunk<T, MODE, CPT>(y, in.row[u], g.N, c.cm, k, o, in.ok[u]);
             }
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws,
@@ -201,17 +255,26 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
 
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const bool live = tile < c.t_end;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
+            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
         }
+    };
+    auto body = [&](const In& in) {
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
 #pragma unroll
@@ -220,23 +283,24 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
                     const int e = k * V + v;
-                    const float xv = xr[u].get(k, v), gv = gr[u].get(k, v);
+                    const float xv = in.xr[u].get(k, v), gv = in.gr[u].get(k, v);
                     const TanhSech2 ts = tanh_sech2(alpha * xv);
                     // alpha * sech^2 is 0 wherever sech^2 is 0 (alpha = +inf would give inf * 0).
                     const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
                     const float d = gv * ga[e];
                     // Contributions of padded rows and columns are dropped after the arithmetic:
                     // a padded x = 0 with alpha = +inf makes NaN, which must not reach a sum.
-                    const bool live = ok[u] && c.cm.valid(k, v, g.N);
+                    const bool live = in.ok[u] && c.cm.valid(k, v, g.N);
                     acc_g[e] += live ? gv * ts.t : 0.f;
                     acc_b[e] += live ? gv : 0.f;
                     acc_a += live ? d * xv * ts.s : 0.f;
                     o[v] = d * as;
                 }
-                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+                store_chunk<T, MODE, CPT>(dx, in.row[u], g.N, c.cm, k, o, in.ok[u]);
             }
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
     // Partial row c.wg; this workgroup's column block of dgamma | dbeta, and its own dalpha
     // column 2N + cblk (stage 2 adds the ncb dalpha columns together).
     float* out = ws + c.wg * g.ws_rs;
@@ -285,7 +349,7 @@ __device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
     for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta,
               float eps, T* __restrict__ y, float* __restrict__ mean_out,
@@ -298,38 +362,43 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
     float ga[E], be[E];
     load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
     load_param_or<T, PT, MODE, CPT>(beta, 0.f, g.N, c.cm, be);
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
 #pragma unroll
-        for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-        }
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+    };
+    auto body = [&](const In& in) {
         float mu[RT], rs[RT];
-        ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
+        ln_stats<T, MODE, CPT, RT>(in.xr, c.cm, g, eps, red, parity, mu, rs);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            if (!ok[u]) continue;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 float o[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    o[v] = __builtin_fmaf((xr[u].get(k, v) - mu[u]) * rs[u], ga[k * V + v], be[k * V + v]);
-                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+                    o[v] = __builtin_fmaf((in.xr[u].get(k, v) - mu[u]) * rs[u], ga[k * V + v], be[k * V + v]);
+                store_chunk<T, MODE, CPT>(y, in.row[u], g.N, c.cm, k, o, in.ok[u]);
             }
-            if (c.lane == 0) {
-                if (mean_out) mean_out[row[u]] = mu[u];
-                if (rstd_out) rstd_out[row[u]] = rs[u];
+            if (in.ok[u] && c.lane == 0) {
+                if (mean_out) mean_out[in.row[u]] = mu[u];
+                if (rstd_out) rstd_out[in.row[u]] = rs[u];
             }
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
               const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
@@ -347,21 +416,40 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_g[e] = acc_b[e] = 0.f;
 
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
+        float mu[RT], rs[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const bool live = tile < c.t_end;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
+        const Rsrc sm = stats_src(mean_in, row0, g.M, live && have_stats);
+        const Rsrc sr = stats_src(rstd_in, row0, g.M, live && have_stats);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
+            in.mu[u] = load_stat(sm, in.row[u], row0, in.ok[u]);
+            in.rs[u] = load_stat(sr, in.row[u], row0, in.ok[u]);
+        }
+    };
+    auto body = [&](const In& in) {
+        const auto& xr = in.xr;
+        const auto& gr = in.gr;
+        const auto& ok = in.ok;
+        const auto& row = in.row;
         float mu[RT], rs[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
-            if (have_stats) {
-                mu[u] = ok[u] ? mean_in[row[u]] : 0.f;
-                rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
-            }
+            mu[u] = in.mu[u];
+            rs[u] = in.rs[u];
         }
         if (!have_stats) ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
         float s[2 * RT];
@@ -398,10 +486,11 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     acc_b[e] += live ? gv : 0.f;
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
-                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+                store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);
             }
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
     float* out = ws + c.wg * g.ws_rs;
     write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
     write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
@@ -431,7 +520,7 @@ __device__ __forceinline__ void rms_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
     for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps,
                T* __restrict__ y, float* __restrict__ rstd_out, Geom g) {
@@ -442,21 +531,28 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
     load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
 #pragma unroll
-        for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-        }
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+    };
+    auto body = [&](const In& in) {
+        const auto& xr = in.xr;
+        const auto& ok = in.ok;
+        const auto& row = in.row;
         float rs[RT];
         rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            if (!ok[u]) continue;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 float o[V];
@@ -465,14 +561,15 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
 #pragma unroll
                 for (int v = 0; v < V; ++v)
                     o[v] = w[k * V + v] * round_through<T>(xr[u].get(k, v) * rs[u]);
-                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o);
+                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o, ok[u]);
             }
-            if (c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
+            if (ok[u] && c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                const PT* __restrict__ weight, float eps, T* __restrict__ dx,
@@ -489,19 +586,36 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_w[e] = 0.f;
 
-    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+    struct In {
         RowRegs<T, MODE, CPT> xr[RT], gr[RT];
-        bool ok[RT];
         int64_t row[RT];
+        int64_t row0;
+        bool ok[RT];
         float rs[RT];
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        c.tile_rows(tile, g, in.row, in.ok);
+        const int64_t row0 = tile * c.rows_per_tile;
+        in.row0 = row0;
+        const bool live = tile < c.t_end;
+        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
+        const Rsrc sr = stats_src(rstd_in, row0, g.M, live);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            row[u] = c.row(tile, u, g);
-            ok[u] = row[u] < g.M;
-            load_row<T, MODE, CPT>(x, row[u], g.N, g.M * g.N, c.cm, ok[u], xr[u]);
-            load_row<T, MODE, CPT>(dy, row[u], g.N, g.M * g.N, c.cm, ok[u], gr[u]);
-            if (rstd_in) rs[u] = ok[u] ? rstd_in[row[u]] : 0.f;
+            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
+            in.rs[u] = load_stat(sr, in.row[u], row0, in.ok[u]);
         }
+    };
+    auto body = [&](const In& in) {
+        const auto& xr = in.xr;
+        const auto& gr = in.gr;
+        const auto& ok = in.ok;
+        const auto& row = in.row;
+        float rs[RT];
+#pragma unroll
+        for (int u = 0; u < RT; ++u) rs[u] = in.rs[u];
         if (!rstd_in) rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
         float s[RT];
 #pragma unroll
@@ -535,10 +649,11 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     acc_w[e] += (ok[u] && c.cm.valid(k, v, g.N)) ? term : 0.f;
                     o[v] = rs[u] * (gg - h * cc);
                 }
-                if (ok[u]) store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o);
+                store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);
             }
         }
-    }
+    };
+    tile_loop<PF != 0, In>(c, fetch, body);
     float* out = ws + c.wg * g.ws_rs;
     write_partial<T, MODE, CPT>(out, g.ws_cs, acc_w, c.cm, c.slot, c.lane, g, part);
 }

@@ -164,6 +164,9 @@ def test_plan_uses_narrow_tiles_for_narrow_rows():
     for bwd in (False, True):
         p = rwn.plan("layernorm", bwd, 401408, 24, torch.float32, cus=256)
         assert p["strided"] and p["grid"] * p["block"] // 64 >= 8 * 256 and p["grid"] % 8 == 0
+    # the persistent grid gives every workgroup the same number of tiles where it can
+    p = rwn.plan("layernorm", False, 401408, 24, torch.float32, cus=256)
+    assert p["ntiles"] % p["grid"] == 0 and p["grid"] % 256 == 0, p
     # short input: the tile count caps the grid (no full grid for one row)
     p = rwn.plan("rmsnorm", False, 1, 128, torch.bfloat16, cus=256)
     assert p["grid"] == 1 and p["ntiles"] == 1
@@ -192,12 +195,17 @@ for layer in ("dyt", "layernorm", "rmsnorm"):
                     cap = 256 if p["rt"] > 1 else (512 if p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2) else 1024)
                     if p["block"] > cap or p["block"] != p["tpr"] * p["rpp"]:
                         bad.append((layer, str(dt), N, mis, bwd, p))
+                    if p["prefetch"] and p["cpt"] * p["rt"] > 2:     # no pipelined form
+                        bad.append(("prefetch", layer, str(dt), N, mis, bwd, p))
+                    if p["strided"] and p["grid"] * ((p["block"] + 63) // 64) > 32 * 256:
+                        bad.append(("waves", layer, str(dt), N, mis, bwd, p))
 print("BAD", bad)
 """
 
 
 @pytest.mark.parametrize("env", ["RWN_WIDE_BLOCK=1024", "RWN_WIDE_BLOCK=64", "RWN_FWD_RT=4", "RWN_BWD_RT=2",
-                                 "RWN_MIN_WAVES=32", "RWN_WINDOW_KB=64", "RWN_BLOCKED_K=3"])
+                                 "RWN_MIN_WAVES=32", "RWN_WG_PER_CU=3", "RWN_BLOCKED_K=3", "RWN_PREFETCH=1",
+                                 "RWN_PREFETCH=0", "RWN_X=0"])
 def test_plans_respect_kernel_launch_bounds_under_tuning_overrides(env):
     """Every plan's workgroup fits the launch bound its kernel was compiled for, also with the
     tuning overrides set (a plan over the bound would fail to launch)."""
