@@ -207,6 +207,15 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
 
 hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
                             int64_t N, void* out0, void* out1, void* out2, hipStream_t s) {
+    if (rs == 1) {
+        // Column-major partials: one workgroup per output column (2N + 1 of them at most).
+        const unsigned grid = (unsigned)(ng < 2 * N + 1 ? ng : 2 * N + 1);
+        if (pdt == DT_F32)
+            return launch(colreduce_cm_kernel<float>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+                          (float*)out0, (float*)out1, (float*)out2);
+        return launch(colreduce_cm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+                      (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
+    }
     const int block = 512;
     // Lanes per column: enough that each lane adds ~8 partial rows (column-major partials) or
     // ~16 (row-major, where lanes of one column are not contiguous).

@@ -710,4 +710,44 @@ colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs
     }
 }
 
+// Stage 2 for column-major partials (rs == 1: column c is ws[c * cs .. c * cs + P)), the
+// layout of short rows.  One workgroup per output column: thread t adds partial rows t,
+// t + blockDim, ... in order in float64 (all of its loads issued up front), the wave sums
+// are formed by a fixed xor butterfly, and thread 0 adds the wave sums in wave order.  The
+// dalpha output (column 2N) adds its ncb partial columns [2N, ng) one after another.
+template <typename PT>
+__global__ void __launch_bounds__(256)
+colreduce_cm_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t cs, int64_t N,
+                    PT* __restrict__ out0, PT* __restrict__ out1, PT* __restrict__ out2) {
+    __shared__ double wsum[4];
+    const int64_t col = blockIdx.x;
+    const int64_t c_end = col == 2 * N ? ng : col + 1;
+    double acc = 0.0;
+    for (int64_t cc = col; cc < c_end; ++cc) {
+        const float* base = ws + cc * cs;
+        int64_t p = threadIdx.x;
+        for (; p + 3 * 256 < P; p += 4 * 256) {
+            const float a0 = base[p], a1 = base[p + 256], a2 = base[p + 512], a3 = base[p + 768];
+            acc += a0; acc += a1; acc += a2; acc += a3;
+        }
+        for (; p < P; p += 256) acc += base[p];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = wsum[0];
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) s += wsum[w];
+        const PT v = from_f32<PT>((float)s);
+        if (col < N) {
+            if (out0) out0[col] = v;
+        } else if (col < 2 * N) {
+            if (out1) out1[col - N] = v;
+        } else {
+            if (out2) out2[0] = v;
+        }
+    }
+}
+
 }  // namespace rwn
