@@ -163,11 +163,14 @@ rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream
  *  elements per chunk, row tiles per workgroup (0 when strided), strided (1: workgroup w
  *  visits tiles w, w + workgroups / column blocks, ...), column blocks per row, XCD remap
  *  (1: workgroup numbers renumbered so consecutive ones share an XCD), prefetch (1: the next
- *  tile's loads are issued before the current tile is processed)}.  misalign_bytes is the
- * common address of x/y/dy/dx modulo 16; cus is the compute-unit count to plan for (0: query
- * the current device). */
+ *  tile's loads are issued before the current tile is processed)}.  param_dtype: the parameter
+ * dtype of a forward (-1: any; a backward is always planned for every parameter dtype, as its
+ * workspace is).  misalign_bytes is the common address of x/y/dy/dx modulo 16.  cus: 0 plans
+ * for the current device exactly as the entry points do (its CU count, and the workgroups of
+ * the chosen kernel that fit on one CU at once); any other value plans for that many CUs from
+ * launch bounds alone, without touching a device. */
 rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
-                    int misalign_bytes, int cus, int64_t* out);
+                    int param_dtype, int misalign_bytes, int cus, int64_t* out);
 
 #ifdef __cplusplus
 }

@@ -268,13 +268,14 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
 
 
 def plan(layer: str, backward: bool, M: int, N: int, dtype: torch.dtype, misalign_bytes: int = 0,
-         cus: int = 0):
-    """The launch plan the library picks.  cus = 0 plans for the current device; any other value
-    plans for that many compute units without touching a device."""
+         cus: int = 0, param_dtype: Optional[torch.dtype] = None):
+    """The launch plan the library picks.  cus = 0 plans for the current device, as the entry
+    points do; any other value plans for that many compute units without touching a device."""
     lib = _L()
     out = (ctypes.c_int64 * 14)()
     li = {"dyt": 0, "layernorm": 1, "rmsnorm": 2}[layer]
-    _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], misalign_bytes, cus, out))
+    pd = -1 if param_dtype is None else _DT[param_dtype]
+    _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], pd, misalign_bytes, cus, out))
     keys = ("mode", "cpt", "rt", "tpr", "rpp", "block", "grid", "ntiles", "vec", "kt", "strided", "ncb", "xcd_remap",
             "prefetch")
     return dict(zip(keys, [int(v) for v in out]))

@@ -39,7 +39,7 @@ SIGNATURES = {
     "rwn_trace_begin": (_ci, [_ci]),
     "rwn_trace_end": (_ci, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int), _ci]),
     "rwn_copy_probe": (_ci, [_vp, _vp, _sz, _vp]),
-    "rwn_plan": (_ci, [_ci, _ci, _i64, _i64, _ci, _ci, _ci, ctypes.POINTER(_i64)]),
+    "rwn_plan": (_ci, [_ci, _ci, _i64, _i64, _ci, _ci, _ci, _ci, ctypes.POINTER(_i64)]),
 }
 
 

@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
@@ -37,8 +39,35 @@ static int env_int(const char* name, int lo, int hi, int dflt) {
     return (k >= lo && k <= hi) ? k : dflt;
 }
 
-bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misalign_bytes,
-               int cus, Plan* out) {
+int kernel_occupancy(const void* kernel, int block, size_t dyn_lds) {
+    struct Key {
+        const void* k;
+        int block;
+        size_t lds;
+        int n;
+    };
+    static std::mutex mu;
+    static std::vector<Key> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Key& e : cache)
+        if (e.k == kernel && e.block == block && e.lds == dyn_lds) return e.n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, dyn_lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    cache.push_back(Key{kernel, block, dyn_lds, n});
+    return n;
+}
+
+static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pdt) {
+    if (layer == LAYER_DYT) return resident_wgs_dyt(backward, p, xdt, pdt);
+    if (layer == LAYER_LN) return resident_wgs_ln(backward, p, xdt, pdt);
+    return resident_wgs_rms(backward, p, xdt, pdt);
+}
+
+bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
+               int cus, bool occupancy, Plan* out) {
     static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
     static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 1);
     static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
@@ -146,6 +175,24 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
     if (p.block > maxb) return false;
     const int64_t rows_per_tile = (int64_t)p.rpp * p.rt;
     p.ntiles = (M + rows_per_tile - 1) / rows_per_tile;
+    if (backward && p.rpp > 1) {   // LDS for combining the row slots' partials
+        int64_t e = (int64_t)p.cpt * v_elems * p.block;
+        if (p.mode == MODE_SHIFTED && N > e) e = N;
+        p.lds_bytes = (size_t)e * sizeof(float);
+    }
+    // Workgroups of this kernel that fit on a CU at once: every workgroup of a persistent grid
+    // must be resident, or the ones that are not start only when others finish.  With pdt = -1
+    // the plan holds for every parameter dtype (the most restrictive kernel decides).
+    int64_t occ = 0;
+    if (occupancy) {
+        const int pdts[2] = {DT_F32, DT_BF16};
+        for (int i = 0; i < 2; ++i) {
+            if (pdt >= 0 && pdts[i] != pdt) continue;
+            if (xdt == DT_F32 && pdts[i] == DT_BF16) continue;   // no such pair
+            const int n = resident_wgs(layer, backward, p, xdt, pdts[i]);
+            if (n > 0) occ = occ == 0 ? n : std::min<int64_t>(occ, n);
+        }
+    }
 
     if (blocked) {
         p.kt = blocked_k;
@@ -159,9 +206,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         // fewer waves.  With ncb column blocks the grid is ncb workgroups per tile stride.
         p.strided = 1;
         const int64_t waves_per_wg = (p.block + 63) / 64;
-        const int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
+        int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
+        if (occ > 0) c_max = std::min(c_max, occ);
         const int64_t c_lo = std::min(c_max, std::max<int64_t>(1, (min_waves + waves_per_wg - 1) / waves_per_wg));
-        const int64_t c_hi = std::max<int64_t>(c_lo, 28 / waves_per_wg);
+        const int64_t c_hi = std::max<int64_t>(c_lo, std::min<int64_t>(c_max, 28 / waves_per_wg));
         int64_t gt = 0;
         double best = -1.0;
         for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
@@ -194,11 +242,6 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misa
         } else {
             p.ws_rs = ng;
             p.ws_cs = 1;
-        }
-        if (p.rpp > 1) {
-            int64_t e = (int64_t)p.cpt * v_elems * p.block;
-            if (p.mode == MODE_SHIFTED && N > e) e = N;
-            p.lds_bytes = (size_t)e * sizeof(float);
         }
     }
     *out = p;

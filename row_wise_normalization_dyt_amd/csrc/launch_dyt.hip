@@ -43,4 +43,24 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
     });
 }
 
+int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt) {
+    int n = 0;
+    (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+            if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
+            else {
+                constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
+                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
+                const void* k = backward ? (const void*)dyt_bwd_kernel<T, PT, M_, C_, R_, P_>
+                                         : (const void*)dyt_fwd_kernel<T, PT, M_, C_, R_, P_>;
+                n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
+                return hipSuccess;
+            }
+        });
+    });
+    return n;
+}
+
 }  // namespace rwn

@@ -134,11 +134,13 @@ hipError_t traced(int tag, hipStream_t s, F&& launch) {
 }
 
 rwn_status plan_for(const char* fn, int layer, bool bwd, int64_t M, int64_t N, rwn_dtype xdt,
-                    int misalign, Plan* p) {
+                    rwn_dtype pdt, int misalign, Plan* p) {
     int cus = 0;
     rwn_status st = device_cus(&cus);
     if (st != RWN_OK) return st;
-    if (!make_plan(layer, bwd, M, N, (int)xdt, misalign, cus, p))
+    // The backward's grid is also its workspace's row count: it is planned for every parameter
+    // dtype at once, exactly as the workspace query plans it.
+    if (!make_plan(layer, bwd, M, N, (int)xdt, bwd ? -1 : (int)pdt, misalign, cus, true, p))
         return fail(RWN_ERR_UNSUPPORTED,
                     "%s: N = %lld with operands %d bytes past a 16-byte boundary needs more than "
                     "1024 threads per row; use 16-byte-aligned operands and N a multiple of %d",
@@ -165,7 +167,7 @@ rwn_status workspace_size(int layer, int64_t M, int64_t N, rwn_dtype xdt, size_t
     for (int mis = 0; mis < 16; mis += esz) {
         Plan p;
         // a misalignment with no plan is rejected by the backward itself
-        if (!make_plan(layer, true, M, N, (int)xdt, mis, cus, &p)) continue;
+        if (!make_plan(layer, true, M, N, (int)xdt, -1, mis, cus, true, &p)) continue;
         const size_t need = (size_t)p.partial_rows() * (size_t)partial_cols(layer, N, p.ncb) * sizeof(float);
         if (need > most) most = need;
     }
@@ -211,7 +213,7 @@ RWN_API rwn_status dyt_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtyp
     int mis = 0;
     if ((st = check_operands(fn, x_dtype, ops, names, 2, &mis)) != RWN_OK) return st;
     Plan p;
-    if ((st = plan_for(fn, LAYER_DYT, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_DYT, false, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = traced(RWN_K_DYT_FWD, s, [&] {
         return launch_dyt_fwd(p, x_dtype, param_dtype, x, alpha, gamma, beta, y, s);
@@ -236,7 +238,7 @@ RWN_API rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, 
     int mis = 0;
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
-    if ((st = plan_for(fn, LAYER_DYT, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_DYT, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
     if ((st = check_workspace(fn, p, LAYER_DYT, workspace, workspace_bytes)) != RWN_OK) return st;
     float* ws = (float*)workspace;
     hipError_t e = traced(RWN_K_DYT_BWD, s, [&] {
@@ -268,7 +270,7 @@ RWN_API rwn_status layernorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype 
     if (((uintptr_t)mean % 4) || ((uintptr_t)rstd % 4))
         return fail(RWN_ERR_INVALID_ARG, "%s: mean/rstd must be float aligned", fn);
     Plan p;
-    if ((st = plan_for(fn, LAYER_LN, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_LN, false, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = traced(RWN_K_LN_FWD, s, [&] {
         return launch_ln_fwd(p, x_dtype, param_dtype, x, gamma, beta, eps, y, mean, rstd, s);
@@ -296,7 +298,7 @@ RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void
     int mis = 0;
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
-    if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
     if ((st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
     float* ws = (float*)workspace;
     hipError_t e = traced(RWN_K_LN_BWD, s, [&] {
@@ -327,7 +329,7 @@ RWN_API rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_
     if ((st = check_operands(fn, x_dtype, ops, names, 2, &mis)) != RWN_OK) return st;
     if ((uintptr_t)rstd % 4) return fail(RWN_ERR_INVALID_ARG, "%s: rstd must be float aligned", fn);
     Plan p;
-    if ((st = plan_for(fn, LAYER_RMS, false, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_RMS, false, M, N, x_dtype, weight_dtype, mis, &p)) != RWN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = traced(RWN_K_RMS_FWD, s, [&] {
         return launch_rms_fwd(p, x_dtype, weight_dtype, x, weight, eps, y, rstd, s);
@@ -353,7 +355,7 @@ RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* 
     int mis = 0;
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
-    if ((st = plan_for(fn, LAYER_RMS, true, M, N, x_dtype, mis, &p)) != RWN_OK) return st;
+    if ((st = plan_for(fn, LAYER_RMS, true, M, N, x_dtype, weight_dtype, mis, &p)) != RWN_OK) return st;
     if ((st = check_workspace(fn, p, LAYER_RMS, workspace, workspace_bytes)) != RWN_OK) return st;
     float* ws = (float*)workspace;
     hipError_t e = traced(RWN_K_RMS_BWD, s, [&] {
@@ -443,7 +445,7 @@ RWN_API rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void
 }
 
 RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
-                            int misalign_bytes, int cus, int64_t* out) {
+                            int param_dtype, int misalign_bytes, int cus, int64_t* out) {
     const char* fn = "rwn_plan";
     if (!out) return fail(RWN_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (layer < 0 || layer > 2) return fail(RWN_ERR_INVALID_ARG, "%s: layer must be 0, 1 or 2", fn);
@@ -453,9 +455,16 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
     if (misalign_bytes < 0 || misalign_bytes >= 16 || misalign_bytes % esz)
         return fail(RWN_ERR_INVALID_ARG, "%s: misalign_bytes must be a multiple of the element size below 16", fn);
     if (cus < 0) return fail(RWN_ERR_INVALID_ARG, "%s: cus must be >= 0", fn);
-    if (cus == 0 && (st = device_cus(&cus)) != RWN_OK) return st;
+    if (param_dtype != -1 && param_dtype != RWN_F32 && param_dtype != RWN_BF16)
+        return fail(RWN_ERR_INVALID_ARG, "%s: param_dtype must be -1, RWN_F32 or RWN_BF16", fn);
+    if (x_dtype == RWN_F32 && param_dtype == RWN_BF16)
+        return fail(RWN_ERR_UNSUPPORTED, "%s: float32 x with bfloat16 parameters is not supported", fn);
+    const bool device = cus == 0;
+    if (device && (st = device_cus(&cus)) != RWN_OK) return st;
     Plan p;
-    if (!make_plan(layer, backward != 0, M, N, (int)x_dtype, misalign_bytes, cus, &p))
+    // As the entry points plan: a backward for every parameter dtype at once.
+    const int pd = backward ? -1 : param_dtype;
+    if (!make_plan(layer, backward != 0, M, N, (int)x_dtype, pd, misalign_bytes, cus, device, &p))
         return fail(RWN_ERR_UNSUPPORTED, "%s: no launch plan for N = %lld", fn, (long long)N);
     out[0] = p.mode; out[1] = p.cpt; out[2] = p.rt; out[3] = p.tpr; out[4] = p.rpp;
     out[5] = p.block; out[6] = p.grid; out[7] = p.ntiles;

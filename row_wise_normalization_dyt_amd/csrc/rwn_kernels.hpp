@@ -170,8 +170,43 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t c
         for (int64_t j = threadIdx.x; j < g.N; j += nb) out[j * cs] = part[j];
         return;
     }
-    // Slots share one column map: a fixed binary tree over the slots, every thread taking part
-    // (slot s adds slot s + st for st = P/2, P/4, ..., 1, P the power of two >= rpp).
+    if (g.tpr < 64) {
+        // Narrow rows: the 64 / tpr slots of a wave share one column map.  An xor butterfly over
+        // lane offsets tpr, 2 tpr, ..., 32 leaves every lane with the wave's sum for its columns
+        // (both partners of each step add the same two values, so they hold identical bits);
+        // then one LDS round adds the waves' sums in wave order.
+        const int nw = (nb + 63) >> 6;
+        const int wl = nb < 64 ? nb : 64;
+        float v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = acc[e];
+        for (int off = g.tpr; off < wl; off <<= 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] += __shfl_xor(v[e], off, 64);
+        }
+        const int wave = threadIdx.x >> 6;
+        __syncthreads();   // previous users of `part` are done
+        if ((threadIdx.x & 63) < g.tpr) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) part[(wave * g.tpr + lane) * E + e] = v[e];
+        }
+        __syncthreads();
+        if (threadIdx.x < g.tpr) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+#pragma unroll
+                for (int vv = 0; vv < V; ++vv) {
+                    const int e = k * V + vv;
+                    float sum = part[lane * E + e];
+                    for (int w = 1; w < nw; ++w) sum += part[(w * g.tpr + lane) * E + e];
+                    if (cm.valid(k, vv, g.N)) out[(int64_t)(cm.col0[k] + vv) * cs] = sum;
+                }
+        }
+        return;
+    }
+    // Wide rows: slots are whole waves with one column map; a fixed binary tree over the slots,
+    // every thread taking part (slot s adds slot s + st for st = P/2, P/4, ..., 1, P the power of
+    // two >= rpp).
     __syncthreads();   // previous users of `part` are done
 #pragma unroll
     for (int e = 0; e < E; ++e) part[e * nb + threadIdx.x] = acc[e];

@@ -41,9 +41,21 @@ struct Plan {
 };
 
 // Plan for one call.  misalign_bytes: address of the [M, N] operands modulo 16 (a multiple of
-// the element size).  cus: compute units of the device.  Returns false if N is too wide.
-bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int misalign_bytes,
-               int cus, Plan* out);
+// the element size).  cus: compute units of the device.  pdt: the parameter dtype, or -1 when
+// the plan must hold for every parameter dtype of x's dtype (the workspace query).  occupancy:
+// ask the runtime how many workgroups of the chosen kernel fit on a CU (needs a current device;
+// false plans from launch bounds alone).  Returns false if N is too wide.
+bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
+               int cus, bool occupancy, Plan* out);
+
+// Workgroups of the plan's kernel that fit on one CU at once (registers, LDS, wave slots), from
+// the runtime; 0 if unknown.  One function per layer, defined beside that layer's launchers.
+int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt);
+int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt);
+int resident_wgs_rms(bool backward, const Plan& p, int xdt, int pdt);
+
+// hipOccupancyMaxActiveBlocksPerMultiprocessor for one kernel, cached (0 on failure).
+int kernel_occupancy(const void* kernel, int block, size_t dyn_lds);
 
 // Partial-row columns of a backward: 2N + ncb (DyT: dgamma | dbeta | one dalpha column per
 // column block), 2N (LayerNorm), N (RMSNorm).
