@@ -31,7 +31,8 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
 //   RWN_XCD_REMAP           0: keep hardware workgroup numbering (default 1: XCD-contiguous)
-//   RWN_PREFETCH            0 / 1: force the plain / pipelined tile loop where both exist
+//   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
+//                           they exist
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -75,7 +76,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
     static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, 1);
-    static const int prefetch = env_int("RWN_PREFETCH", 0, 1, -1);
+    static const int prefetch = env_int("RWN_PREFETCH", 0, 2, -1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -161,9 +162,13 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // the SHIFTED LayerNorm / RMSNorm ones) and in 16-wave rows, and in SHIFTED backwards;
     // elsewhere the doubled input registers cost more than the overlap gains.  Shapes with
     // more than two chunks per thread have no pipelined form.
+    // Narrow DyT rows (the most arithmetic per byte) gain from running two tiles ahead: in the
+    // backward always, in the forward from 16 lanes per row up.
     if (p.cpt * p.rt <= 2) {
         const bool one = p.cpt * p.rt == 1;
-        if (prefetch >= 0) p.pf = prefetch;
+        const bool narrow_dyt = layer == LAYER_DYT && one && p.mode == MODE_ALIGNED && p.tpr <= 64;
+        if (prefetch >= 0) p.pf = (prefetch == 2 && !(one && p.mode != MODE_SCALAR)) ? 1 : prefetch;
+        else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
         else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
         else p.pf = (p.mode == MODE_SHIFTED && one) ? 1 : 0;
     }

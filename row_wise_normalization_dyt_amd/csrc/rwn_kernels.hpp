@@ -88,19 +88,35 @@ struct RowCtx {
     }
 };
 
-// Software pipelining of the tile loop (kernel parameter PF, chosen by the planner).  With PF
-// the loads of the next tile are issued before the current tile is reduced, computed and
-// stored, so every wave keeps two tiles of loads in flight and the store of one tile overlaps
-// the load of the next; the registers holding a tile's inputs are doubled.  Only shapes with
-// at most two 16-byte chunks per thread per tensor have the pipelined form.
+// Software pipelining of the tile loop (kernel parameter PF, chosen by the planner).  With
+// PF = 1 the loads of the next tile are issued before the current tile is reduced, computed
+// and stored, so every wave keeps two tiles of loads in flight and the store of one tile
+// overlaps the load of the next; the registers holding a tile's inputs are doubled.  Only
+// shapes with at most two 16-byte chunks per thread per tensor have that form.  PF = 2 runs
+// two tiles ahead (three buffers), for one chunk per thread.
 
 // Runs body(in) for every tile of the workgroup in order; fetch(tile, in) issues the tile's
 // loads (a tile past the workgroup's range loads nothing).  The pipelined form alternates two
 // buffers instead of copying the next tile into the current one: a register copy would have
 // to wait for the loads it copies and so end the overlap.
-template <bool PF, typename In, typename Ctx, typename Fetch, typename Body>
+template <int PF, typename In, typename Ctx, typename Fetch, typename Body>
 __device__ __forceinline__ void tile_loop(const Ctx& c, Fetch&& fetch, Body&& body) {
-    if constexpr (PF) {
+    if constexpr (PF == 2) {
+        // two tiles ahead: three buffers in rotation
+        In a, b, d;
+        fetch(c.t_begin, a);
+        fetch(c.t_begin + c.t_step, b);
+        for (int64_t tile = c.t_begin; tile < c.t_end; tile += 3 * c.t_step) {
+            fetch(tile + 2 * c.t_step, d);
+            body(a);
+            if (tile + c.t_step >= c.t_end) break;
+            fetch(tile + 3 * c.t_step, a);
+            body(b);
+            if (tile + 2 * c.t_step >= c.t_end) break;
+            fetch(tile + 4 * c.t_step, b);
+            body(d);
+        }
+    } else if constexpr (PF == 1) {
         In a, b;
         fetch(c.t_begin, a);
         for (int64_t tile = c.t_begin; tile < c.t_end; tile += 2 * c.t_step) {
@@ -270,7 +286,7 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
             }
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
@@ -335,7 +351,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
             }
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
     // Partial row c.wg; this workgroup's column block of dgamma | dbeta, and its own dalpha
     // column 2N + cblk (stage 2 adds the ncb dalpha columns together).
     float* out = ws + c.wg * g.ws_rs;
@@ -430,7 +446,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
             }
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
@@ -525,7 +541,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
             }
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
     float* out = ws + c.wg * g.ws_rs;
     write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
     write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
@@ -601,7 +617,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
             if (ok[u] && c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
 }
 
 template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
@@ -688,7 +704,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
             }
         }
     };
-    tile_loop<PF != 0, In>(c, fetch, body);
+    tile_loop<PF, In>(c, fetch, body);
     float* out = ws + c.wg * g.ws_rs;
     write_partial<T, MODE, CPT>(out, g.ws_cs, acc_w, c.cm, c.slot, c.lane, g, part);
 }

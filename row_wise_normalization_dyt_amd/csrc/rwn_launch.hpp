@@ -30,7 +30,8 @@ struct Plan {
     int strided = 0;          // 1: grid-stride over tiles (grid * rpp a multiple of V)
     int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
     int xcd_remap = 0;        // renumber workgroups XCD-contiguously (needs grid % 8 == 0)
-    int pf = 0;               // software-pipelined tile loop (only shapes with cpt * rt <= 2)
+    int pf = 0;               // software-pipelined tile loop: 0 off, 1 one tile ahead (cpt * rt <= 2),
+                              // 2 two tiles ahead (cpt * rt == 1, vector modes)
     int base_shift = 0;       // SHIFTED: base misalignment in elements
     int64_t ws_rs = 0;        // backward partials: element (p, c) at ws[p * ws_rs + c * ws_cs]
     int64_t ws_cs = 0;
@@ -100,20 +101,27 @@ hipError_t dispatch_pf(const Plan& p, F&& f) {
     return p.pf ? f(IC<1>{}) : f(IC<0>{});
 }
 
+// One chunk, one row per thread: the two-tile-deep pipeline (PF = 2) exists as well.
+template <typename F>
+hipError_t dispatch_pf2(const Plan& p, F&& f) {
+    return p.pf == 2 ? f(IC<2>{}) : p.pf ? f(IC<1>{}) : f(IC<0>{});
+}
+
 template <typename T, typename F>
 hipError_t dispatch_shape(const Plan& p, F&& f) {
-    if (p.pf && p.cpt * p.rt > 2) return hipErrorInvalidValue;
+    if ((p.pf && p.cpt * p.rt > 2) || (p.pf == 2 && (p.cpt * p.rt != 1 || p.mode == MODE_SCALAR)))
+        return hipErrorInvalidValue;
     if (p.mode == MODE_ALIGNED) {
         if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{}, IC<0>{});
         if (p.rt == 2 && p.cpt == 1)
             return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{}, pf); });
         if (p.rt == 1) {
-            if (p.cpt == 1) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf); });
+            if (p.cpt == 1) return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf); });
             if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{}, pf); });
             if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{}, IC<0>{});
         }
     } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
-        if (p.cpt == 1) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf); });
+        if (p.cpt == 1) return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf); });
         if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{}, pf); });
         if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{}, IC<0>{});
     } else if (p.mode == MODE_SCALAR && p.rt == 1) {
