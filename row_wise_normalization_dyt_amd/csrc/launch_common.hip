@@ -31,6 +31,7 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
 //   RWN_XCD_REMAP           0: keep hardware workgroup numbering (default 1: XCD-contiguous)
+//   RWN_WIDE_CPT            1, 2 or 4: chunks per thread of wide LayerNorm / RMSNorm rows
 //   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
 //                           they exist
 static int env_int(const char* name, int lo, int hi, int dflt) {
@@ -77,6 +78,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
     static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, 1);
     static const int prefetch = env_int("RWN_PREFETCH", 0, 2, -1);
+    static const int wide_cpt = env_int("RWN_WIDE_CPT", 1, 4, 0);
     Plan p;
     p.M = M;
     p.N = N;
@@ -126,14 +128,25 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         // (fewer waves to combine per row).  Wave limits follow the kernels' launch bounds.
         int best_cpt = 0, best_w = 0;
         int64_t best_waste = -1;
-        const int order_dyt[3] = {1, 4, 2}, order_norm[3] = {2, 4, 1};
+        const int order_dyt[3] = {1, 4, 2}, order_norm[3] = {2, 4, 1}, order_few_waves[3] = {4, 2, 1};
         const int* order = layer == LAYER_DYT ? order_dyt : order_norm;
+        // A SHIFTED RMSNorm forward runs fastest with the fewest waves per row (measured at
+        // N = 1025: one wave with four chunks per lane beats three waves with one), idle lanes
+        // notwithstanding: no cross-wave combine, and its one reduction has no masked terms.
+        const bool few_waves = layer == LAYER_RMS && !backward && p.mode == MODE_SHIFTED;
+        if (few_waves) order = order_few_waves;
         for (int oi = 0; oi < 3; ++oi) {
             const int cpt = order[oi];
+            if (wide_cpt > 0 && cpt != wide_cpt) continue;
             const int wmax = (cpt == 1 || (cpt == 4 && esz == 2)) ? 8 : 16;
             const int64_t w = (chunks + 64 * cpt - 1) / (64 * cpt);
             if (w > wmax) continue;
             const int64_t waste = w * 64 * cpt - chunks;
+            if (few_waves) {   // first shape that fits
+                best_cpt = cpt;
+                best_w = (int)w;
+                break;
+            }
             if (best_waste < 0 || waste < best_waste) {
                 best_waste = waste;
                 best_cpt = cpt;
