@@ -220,8 +220,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         // [16, 28] resident waves per CU (fewer waves leave HBM latency exposed; more add
         // nothing).  Within that range the c whose tile count per workgroup is most even wins:
         // the kernel lasts as long as its busiest workgroup, so ntiles / gt against
-        // ceil(ntiles / gt) is the fraction of the machine kept busy to the end.  Ties go to
-        // fewer waves.  With ncb column blocks the grid is ncb workgroups per tile stride.
+        // ceil(ntiles / gt) is the fraction of the machine kept busy to the end.  Each extra
+        // workgroup per CU must buy 2% of balance (measured: narrow LayerNorm backwards at 28
+        // waves per CU run 20% slower than at 20).  With ncb column blocks the grid is ncb
+        // workgroups per tile stride.
         p.strided = 1;
         const int64_t waves_per_wg = (p.block + 63) / 64;
         int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
@@ -237,7 +239,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             if (cand < 8) cand = 8;
             if (cand >= p.ntiles) { gt = p.ntiles; break; }   // one tile per workgroup
             const double per = (double)p.ntiles / (double)cand;
-            const double eff = per / std::ceil(per) - 0.005 * (double)(cc - c_lo);
+            const double eff = per / std::ceil(per) - 0.02 * (double)(cc - c_lo);
             if (eff > best + 1e-9) { best = eff; gt = cand; }
         }
         if (gt == 0) {   // forced c out of range: nearest in-range candidate

@@ -21,7 +21,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rwn {
+
+template <int V> using IC = std::integral_constant<int, V>;
 
 typedef __bf16 bf16_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));

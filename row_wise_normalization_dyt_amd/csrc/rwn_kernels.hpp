@@ -325,31 +325,45 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
             load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
         }
     };
+    // With a finite alpha nothing a padded element computes can be NaN: its x, dy and gamma
+    // read as 0, so z = 0, tanh = 0, sech^2 = 1 and every term it adds is exactly 0.  That case
+    // needs no masks.  With alpha = +-inf a padded x = 0 gives z = inf * 0 = NaN, so those terms
+    // are dropped after the arithmetic, and alpha * sech^2 is taken as 0 where sech^2 is 0.
+    const bool finite_alpha = __builtin_isfinite(alpha);
     auto body = [&](const In& in) {
+        auto rows = [&](auto finite) {
 #pragma unroll
-        for (int u = 0; u < RT; ++u) {
+            for (int u = 0; u < RT; ++u) {
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                float o[V];
+                for (int k = 0; k < CPT; ++k) {
+                    float o[V];
 #pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const int e = k * V + v;
-                    const float xv = in.xr[u].get(k, v), gv = in.gr[u].get(k, v);
-                    const TanhSech2 ts = tanh_sech2(alpha * xv);
-                    // alpha * sech^2 is 0 wherever sech^2 is 0 (alpha = +inf would give inf * 0).
-                    const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
-                    const float d = gv * ga[e];
-                    // Contributions of padded rows and columns are dropped after the arithmetic:
-                    // a padded x = 0 with alpha = +inf makes NaN, which must not reach a sum.
-                    const bool live = in.ok[u] && c.cm.valid(k, v, g.N);
-                    acc_g[e] += live ? gv * ts.t : 0.f;
-                    acc_b[e] += live ? gv : 0.f;
-                    acc_a += live ? d * xv * ts.s : 0.f;
-                    o[v] = d * as;
+                    for (int v = 0; v < V; ++v) {
+                        const int e = k * V + v;
+                        const float xv = in.xr[u].get(k, v), gv = in.gr[u].get(k, v);
+                        const TanhSech2 ts = tanh_sech2(alpha * xv);
+                        const float d = gv * ga[e];
+                        if constexpr (decltype(finite)::value) {
+                            const float ds = d * ts.s;   // dy * gamma * sech^2
+                            acc_g[e] = __builtin_fmaf(gv, ts.t, acc_g[e]);
+                            acc_b[e] += gv;
+                            acc_a = __builtin_fmaf(xv, ds, acc_a);
+                            o[v] = alpha * ds;
+                        } else {
+                            const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
+                            const bool live = in.ok[u] && c.cm.valid(k, v, g.N);
+                            acc_g[e] += live ? gv * ts.t : 0.f;
+                            acc_b[e] += live ? gv : 0.f;
+                            acc_a += live ? d * xv * ts.s : 0.f;
+                            o[v] = d * as;
+                        }
+                    }
+                    store_chunk<T, MODE, CPT>(dx, in.row[u], g.N, c.cm, k, o, in.ok[u]);
                 }
-                store_chunk<T, MODE, CPT>(dx, in.row[u], g.N, c.cm, k, o, in.ok[u]);
             }
-        }
+        };
+        if (finite_alpha) rows(IC<1>{});
+        else rows(IC<0>{});
     };
     tile_loop<PF, In>(c, fetch, body);
     // Partial row c.wg; this workgroup's column block of dgamma | dbeta, and its own dalpha
@@ -503,6 +517,14 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
             rs[u] = in.rs[u];
         }
         if (!have_stats) ln_stats<T, MODE, CPT, RT>(xr, c.cm, g, eps, red, parity, mu, rs);
+        // Padded elements read x = dy = gamma = 0, so every term below is 0 for them as long as
+        // x_hat is finite: a padded row's statistics are zeroed (recomputed ones could be
+        // infinite with eps = 0).  No per-element masks are needed.
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            mu[u] = ok[u] ? mu[u] : 0.f;
+            rs[u] = ok[u] ? rs[u] : 0.f;
+        }
         float s[2 * RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -513,9 +535,8 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                 for (int v = 0; v < V; ++v) {
                     const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
                     const float gg = gr[u].get(k, v) * ga[k * V + v];
-                    const bool cv = c.cm.valid(k, v, g.N);
-                    a += cv ? gg : 0.f;
-                    b += cv ? gg * xh : 0.f;
+                    a += gg;
+                    b = __builtin_fmaf(gg, xh, b);
                 }
             s[2 * u] = a;
             s[2 * u + 1] = b;
@@ -532,9 +553,8 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     const int e = k * V + v;
                     const float gv = gr[u].get(k, v);
                     const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
-                    const bool live = ok[u] && c.cm.valid(k, v, g.N);
-                    acc_g[e] += live ? gv * xh : 0.f;
-                    acc_b[e] += live ? gv : 0.f;
+                    acc_g[e] = __builtin_fmaf(gv, xh, acc_g[e]);
+                    acc_b[e] += gv;
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
                 store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);
@@ -668,6 +688,10 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
 #pragma unroll
         for (int u = 0; u < RT; ++u) rs[u] = in.rs[u];
         if (!rstd_in) rms_stats<T, MODE, CPT, RT>(xr, g, eps, red, parity, rs);
+        // Padded elements read x = dy = 0, so their terms are 0 as long as x * rstd is finite:
+        // a padded row's rstd is zeroed (a recomputed one is infinite with eps = 0).
+#pragma unroll
+        for (int u = 0; u < RT; ++u) rs[u] = ok[u] ? rs[u] : 0.f;
         float s[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -697,7 +721,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     const float gg = round_through<T>(gv * w[e]);
                     // weight-gradient term: dy * n rounded to the weight's dtype before the sum.
                     const float term = round_through<PT>(gv * round_through<T>(h));
-                    acc_w[e] += (ok[u] && c.cm.valid(k, v, g.N)) ? term : 0.f;
+                    acc_w[e] += term;
                     o[v] = rs[u] * (gg - h * cc);
                 }
                 store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);

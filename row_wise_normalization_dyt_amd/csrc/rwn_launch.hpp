@@ -82,7 +82,6 @@ inline Geom make_geom(const Plan& p) {
     return g;
 }
 
-template <int V> using IC = std::integral_constant<int, V>;
 template <typename T> struct TypeTag { using type = T; };
 
 // Calls f(TypeTag<T>, TypeTag<PT>) for the supported dtype pairs.

@@ -78,6 +78,16 @@ def test_backward_without_saved_stats(layer):
     tol.assert_reports(reps)
 
 
+@pytest.mark.parametrize("layer", ["layernorm", "rmsnorm"])
+def test_backward_recomputing_stats_with_zero_eps(layer):
+    """eps = 0 with statistics recomputed in the backward: a padded row's recomputed rstd is
+    infinite there, which must not reach the parameter gradients (ragged tiles at every M)."""
+    reps = []
+    for (M, N) in [(1001, 24), (77, 129), (257, 1025)]:
+        reps += _run_small(layer, M, N, "f32", "f32", use_stats=False, eps=0.0)
+    tol.assert_reports(reps)
+
+
 def test_layernorm_without_affine():
     wl = workloads.small("layernorm", 999, 48, "f32", "f32", seed=5)
     inp = workloads.make_inputs(wl)
