@@ -163,9 +163,17 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
 
     // Row slots: narrow rows fill 256-thread workgroups; wide rows use wide_block threads.
     // SHIFTED slots each carry their own shift, so a strided SHIFTED workgroup has one slot.
-    const bool blocked = backward && blocked_k > 0 && p.ncb == 1;
+    // A blocked SHIFTED workgroup walks consecutive tiles, so its slots must be V rows apart
+    // (rpp = V) for each slot to keep one shift; where V slots do not fit in a workgroup the
+    // backward stays strided.
+    bool blocked = backward && blocked_k > 0 && p.ncb == 1;
     if (p.mode == MODE_SHIFTED) {
-        p.rpp = (blocked && (int64_t)p.tpr * V <= 1024) ? V : 1;
+        if (blocked && (int64_t)p.tpr * V <= max_block(p.rt, p.cpt, esz)) {
+            p.rpp = V;
+        } else {
+            p.rpp = 1;
+            blocked = false;
+        }
     } else {
         const int target = p.tpr <= 64 ? 256 : wide_block;
         p.rpp = p.tpr >= target ? 1 : target / p.tpr;
@@ -188,7 +196,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // Keep to the kernel shape's launch bound (tpr itself always fits: see the wave limits).
     const int maxb = max_block(p.rt, p.cpt, esz);
     if (p.tpr * p.rpp > maxb) p.rpp = maxb / p.tpr > 0 ? maxb / p.tpr : 1;
-    if (p.mode == MODE_SHIFTED && p.rpp > 1 && p.rpp % V) p.rpp = 1;
+    if (p.mode == MODE_SHIFTED && p.rpp % V) {
+        p.rpp = 1;
+        blocked = false;
+    }
     p.block = p.tpr * p.rpp;
     if (p.block > maxb) return false;
     const int64_t rows_per_tile = (int64_t)p.rpp * p.rt;

@@ -149,8 +149,8 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
             else:
                 # blocked: consecutive tiles, every tile covered exactly once
                 assert p["grid"] * p["kt"] >= p["ntiles"] > (p["grid"] - 1) * p["kt"]
-                if p["mode"] == 1 and p["rpp"] > 1:
-                    assert p["rpp"] % V == 0, p    # slot s always sees rows = s mod V
+                if p["mode"] == 1 and p["kt"] > 1:
+                    assert p["rpp"] % V == 0, p    # consecutive tiles keep each slot's shift
                 if not backward:
                     assert p["kt"] == 1
 
@@ -203,6 +203,9 @@ for layer in ("dyt", "layernorm", "rmsnorm"):
                         bad.append(("prefetch", layer, str(dt), N, mis, bwd, p))
                     if p["strided"] and p["grid"] * ((p["block"] + 63) // 64) > 32 * 256:
                         bad.append(("waves", layer, str(dt), N, mis, bwd, p))
+                    V = 16 // esz
+                    if p["mode"] == 1 and not p["strided"] and p["kt"] > 1 and p["rpp"] % V:
+                        bad.append(("shift", layer, str(dt), N, mis, bwd, p))   # a slot's rows change shift
 print("BAD", bad)
 """
 

@@ -202,3 +202,38 @@ def test_full_size_workload(name):
     rows = gc.sample_rows(wl.M, k=24)
     reps = gc.check_workload(wl, DEV, rows=rows, on_gpu_inputs=True)
     tol.assert_reports(reps)
+
+
+# ------------------------------------------------------------- tuning overrides keep parity
+
+_OVERRIDE_SCRIPT = r"""
+import sys
+sys.path.insert(0, {root!r})
+import workloads
+from tests import gpu_cases as gc
+bad = []
+for layer in ("dyt", "layernorm", "rmsnorm"):
+    for (M, N, xdt, pdt) in [(4099, 24, "f32", "f32"), (1031, 128, "bf16", "f32"), (130, 2048, "bf16", "bf16"),
+                             (67, 1025, "bf16", "f32"), (33, 4096, "f32", "f32")]:
+        wl = workloads.small(layer, M, N, xdt, pdt, seed=11)
+        print("case:", wl.name, flush=True)
+        bad += [str(r) for r in gc.check_workload(wl, "cuda") if not r.ok()]
+print("BAD", bad, flush=True)
+"""
+
+
+@pytest.mark.parametrize("env", ["RWN_PREFETCH=0", "RWN_PREFETCH=1", "RWN_PREFETCH=2", "RWN_FWD_RT=4 RWN_BWD_RT=2",
+                                 "RWN_WIDE_CPT=4", "RWN_BLOCKED_K=3", "RWN_XCD_REMAP=0 RWN_WG_PER_CU=2"])
+def test_tuning_overrides_keep_parity(env):
+    """The tuning knobs change the launch plan (pipelining depth, rows per thread, chunks per
+    thread, tile assignment, grid); every plan they reach must still match the oracle.  The
+    knobs are read once per process, so each setting runs in a child process."""
+    import os, subprocess, sys
+    _banner("overrides", env)
+    child_env = dict(os.environ)
+    child_env.update(kv.split("=") for kv in env.split())
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-u", "-c", _OVERRIDE_SCRIPT.format(root=root)], env=child_env,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-3000:])
+    assert "BAD []" in r.stdout, r.stdout[-3000:]
