@@ -44,6 +44,9 @@ struct RowCtx {
     ColMap<T, MODE, CPT> cm;
 
     __device__ __forceinline__ RowCtx(const Geom& g) {
+        // Workgroups are whole waves: with rows of tpr lanes packed without wave alignment,
+        // the threads past rpp * tpr form a slot of their own that owns no row (every load
+        // reads zeros, nothing is stored), and take part only in the workgroup's reductions.
         slot = threadIdx.x / g.tpr;
         lane = threadIdx.x - slot * g.tpr;
         // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).  The
@@ -83,7 +86,7 @@ struct RowCtx {
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
             r[u] = row(tile, u, g);
-            ok[u] = tile < t_end && r[u] < g.M;
+            ok[u] = tile < t_end && r[u] < g.M && slot < g.rpp;
         }
     }
 };
@@ -158,6 +161,7 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t c
     constexpr int V = ColMap<T, MODE, CPT>::V;
     constexpr int E = CPT * V;
     if (g.rpp == 1) {
+        if (slot != 0) return;   // the idle slot of a packed workgroup
 #pragma unroll
         for (int k = 0; k < CPT; ++k)
 #pragma unroll

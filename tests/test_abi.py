@@ -129,15 +129,17 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
             assert p["grid"] % p["ncb"] == 0 and (p["ncb"] == 1 or layer == "dyt")
             if p["xcd_remap"]:
                 assert p["grid"] % 8 == 0      # the renumbering is a bijection
-            assert p["block"] == p["tpr"] * p["rpp"] and p["block"] <= 1024 and p["block"] % 64 == 0 or p["block"] < 64
+            packed = layer == "dyt" and p["mode"] == 1 and 64 < p["tpr"] < 512 and p["tpr"] % 64 != 0
+            assert p["block"] <= 1024 and (p["block"] % 64 == 0 or p["block"] < 64), p
+            assert p["block"] == (-(-p["tpr"] * p["rpp"] // 64) * 64 if packed else p["tpr"] * p["rpp"]), p
             # launch bounds: one chunk per thread (and bf16 with four) at most 512 threads
             if p["rt"] == 1 and (p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2)):
                 assert p["block"] <= 512, p
-            assert p["tpr"] <= 64 and (p["tpr"] & (p["tpr"] - 1)) == 0 or p["tpr"] % 64 == 0, p
+            assert p["tpr"] <= 64 and (p["tpr"] & (p["tpr"] - 1)) == 0 or p["tpr"] % 64 == 0 or packed, p
             if p["mode"] == 0:
                 assert N % V == 0 and mis == 0
             if p["mode"] == 1:
-                assert p["rt"] == 1 and (p["rpp"] == 1 or p["rpp"] % V == 0)
+                assert p["rt"] == 1 and (p["rpp"] == 1 or p["rpp"] % V == 0 or packed)
             rows_per_tile = p["rpp"] * p["rt"]
             assert p["ntiles"] * rows_per_tile >= M > (p["ntiles"] - 1) * rows_per_tile
             if p["strided"]:
@@ -197,7 +199,7 @@ for layer in ("dyt", "layernorm", "rmsnorm"):
                     except rwn.RwnError:
                         continue
                     cap = 256 if p["rt"] > 1 else (512 if p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2) else 1024)
-                    if p["block"] > cap or p["block"] != p["tpr"] * p["rpp"]:
+                    if p["block"] > cap or p["block"] < p["tpr"] * p["rpp"] or p["block"] % 64:
                         bad.append((layer, str(dt), N, mis, bwd, p))
                     if p["prefetch"] and p["cpt"] * p["rt"] > 2:     # no pipelined form
                         bad.append(("prefetch", layer, str(dt), N, mis, bwd, p))
