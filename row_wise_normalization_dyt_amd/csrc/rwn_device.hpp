@@ -134,6 +134,8 @@ struct RowRegs {
 // tensor's end (rounded up to 16: the aligned block that holds the last element), capped at
 // 1 GiB -- a tile spans at most 16 rows of 16384 float32, far less.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOutOfRange = 0x80000000u;   // above every record count
 constexpr int64_t kMaxRecords = int64_t(1) << 30;
 constexpr int kBufferFormat = 0x00020000;       // descriptor word 3: 32-bit data format
@@ -203,7 +205,6 @@ __device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_
                                          const ColMap<T, MODE, CPT>& cm, bool rowvalid,
                                          RowRegs<T, MODE, CPT>& r) {
     constexpr int V = RowRegs<T, MODE, CPT>::V;
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const bool in = rowvalid && cm.any[k];
@@ -230,9 +231,107 @@ __device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_
     }
 }
 
-// Store chunk k of row `row` of p (row pitch N) from V float32 values rounded to T; only
-// columns inside the row are written, nothing when `rowvalid` is false.  A whole chunk is one
-// nontemporal 16-byte store; a SHIFTED chunk cut by the row's ends is written element by element.
+// Stores go through the same tile descriptors as the loads (TileSrc of the output tensor).  A
+// store whose offset lies past the record count writes nothing, so a masked lane issues its
+// stores like every other lane, with no branch around them.  That keeps the number of memory
+// operations a wave has issued the same on every path through the loop body, which is what
+// lets the compiler wait for the next tile's loads alone: loads and stores share one in-order
+// counter, and a store count that differs between paths makes it wait for everything,
+// including the stores just issued.
+
+__device__ __forceinline__ void store_b128(const TileSrc& d, bool in, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, d.rsrc, lane_offset(in, off), 0, kNontemporal);
+}
+__device__ __forceinline__ void store_b64(const TileSrc& d, bool in, uint32_t off, uint32_t lo, uint32_t hi) {
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){lo, hi}, d.rsrc, lane_offset(in, off), 0, 0);
+}
+__device__ __forceinline__ void store_b32(const TileSrc& d, bool in, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, d.rsrc, lane_offset(in, off), 0, 0);
+}
+__device__ __forceinline__ void store_b16(const TileSrc& d, bool in, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, d.rsrc, lane_offset(in, off), 0, 0);
+}
+
+__device__ __forceinline__ uint32_t word_at(const u32x4& w, int i) {
+    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+}
+
+// V float32 values rounded to T, packed as the 16 bytes of one chunk.
+template <typename T>
+__device__ __forceinline__ u32x4 pack_chunk(const float* o) {
+    if constexpr (sizeof(T) == 4) {
+        return (u32x4){__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
+                       __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3])};
+    } else {
+        f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+    }
+}
+
+// Store chunk k of row `row` (row pitch N) into the tile destination d, from V float32 values
+// rounded to T; only columns inside the row are written, nothing when `rowvalid` is false.  A
+// whole chunk is one nontemporal 16-byte store.  A SHIFTED chunk cut by the row's ends covers
+// bytes [a, b) of its aligned 16-byte block (the rest belongs to the neighbouring row); that
+// range is written as naturally aligned 2-, 4- and 8-byte pieces: up to three rising from a to
+// the next 16-byte boundary and up to three falling from there to b.  Every lane issues all
+// of these stores, with out-of-range offsets for the pieces it does not need.
+template <typename T, int MODE, int CPT>
+__device__ __forceinline__ void store_chunk(const TileSrc& d, int64_t row, int64_t N,
+                                            const ColMap<T, MODE, CPT>& cm, int k, const float* o,
+                                            bool rowvalid) {
+    constexpr int V = ColMap<T, MODE, CPT>::V;
+    constexpr int ES = (int)sizeof(T);
+    const uint32_t off = (uint32_t)((row * N + cm.col0[k] - d.e0) * (int64_t)ES);
+    if constexpr (MODE == MODE_SCALAR) {
+        const bool in = rowvalid && cm.any[k];
+        if constexpr (ES == 4) store_b32(d, in, off, __builtin_bit_cast(uint32_t, o[0]));
+        else store_b16(d, in, off, (uint32_t)__builtin_bit_cast(unsigned short, from_f32<T>(o[0])));
+    } else {
+        const u32x4 w = pack_chunk<T>(o);
+        store_b128(d, rowvalid && (MODE == MODE_ALIGNED ? cm.any[k] : cm.full[k]), off, w);
+        if constexpr (MODE == MODE_SHIFTED) {
+            const bool cut = rowvalid && cm.any[k] && !cm.full[k];
+            const int j0 = cm.col0[k];
+            const int lo = j0 < 0 ? -j0 : 0;
+            const int hi = (int64_t)j0 + V > N ? (int)(N - j0) : V;
+            int a = cut ? lo * ES : 16;
+            const int b = cut ? hi * ES : 16;
+            if constexpr (ES == 2) {
+                const bool p = (a & 2) && a < b;   // high half of word a / 4
+                store_b16(d, p, off + a, word_at(w, a >> 2) >> 16);
+                a += p ? 2 : 0;
+            }
+            {
+                const bool p = (a & 4) && a + 4 <= b;   // word 1 or 3
+                store_b32(d, p, off + a, (a & 8) ? w[3] : w[1]);
+                a += p ? 4 : 0;
+            }
+            {
+                const bool p = (a & 8) && a + 8 <= b;   // a == 8: words 2, 3
+                store_b64(d, p, off + 8, w[2], w[3]);
+                a += p ? 8 : 0;
+            }
+            {
+                const bool p = b - a >= 8;   // only from a == 0: words 0, 1
+                store_b64(d, p, off, w[0], w[1]);
+                a += p ? 8 : 0;
+            }
+            {
+                const bool p = b - a >= 4;
+                store_b32(d, p, off + a, word_at(w, a >> 2));
+                a += p ? 4 : 0;
+            }
+            if constexpr (ES == 2) {
+                const bool p = b - a >= 2;   // low half of word a / 4
+                store_b16(d, p, off + a, word_at(w, a >> 2) & 0xFFFFu);
+            }
+        }
+    }
+}
+
+// Store chunk k of row `row` of p (row pitch N) with global stores under the row mask: a
+// whole chunk is one nontemporal 16-byte store, a SHIFTED chunk cut by the row's ends is
+// written element by element.
 template <typename T, int MODE, int CPT>
 __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int64_t N,
                                             const ColMap<T, MODE, CPT>& cm, int k, const float* o,
@@ -258,6 +357,22 @@ __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int6
         }
     }
 }
+
+// Which of the two store forms a kernel uses (measured): the branch-free buffer stores pay in
+// backward kernels over wide aligned rows (two or more chunks per lane), whose loops carry
+// the most loads in flight; elsewhere the masked global stores are as fast or faster (their
+// descriptors cost scalar work per tile, and SHIFTED cut chunks take six piece stores).
+template <int MODE, int CPT, bool BWD>
+constexpr bool kBufferStores = BWD && MODE == MODE_ALIGNED && CPT >= 2;
+
+template <typename T, int MODE, int CPT, bool BUF>
+__device__ __forceinline__ void put_chunk(T* __restrict__ p, const TileSrc& d, int64_t row, int64_t N,
+                                          const ColMap<T, MODE, CPT>& cm, int k, const float* o,
+                                          bool rowvalid) {
+    if constexpr (BUF) store_chunk<T, MODE, CPT>(d, row, N, cm, k, o, rowvalid);
+    else store_chunk<T, MODE, CPT>(p, row, N, cm, k, o, rowvalid);
+}
+
 
 // Load a per-column parameter vector for this thread's columns (0 outside [0, N)).
 template <typename T, typename PT, int MODE, int CPT>

@@ -334,7 +334,9 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
     // needs no masks.  With alpha = +-inf a padded x = 0 gives z = inf * 0 = NaN, so those terms
     // are dropped after the arithmetic, and alpha * sech^2 is taken as 0 where sech^2 is 0.
     const bool finite_alpha = __builtin_isfinite(alpha);
+    constexpr bool BUF = kBufferStores<MODE, CPT, true>;
     auto body = [&](const In& in) {
+        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
         auto rows = [&](auto finite) {
 #pragma unroll
             for (int u = 0; u < RT; ++u) {
@@ -362,7 +364,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
                             o[v] = d * as;
                         }
                     }
-                    store_chunk<T, MODE, CPT>(dx, in.row[u], g.N, c.cm, k, o, in.ok[u]);
+                    put_chunk<T, MODE, CPT, BUF>(dx, dst, in.row[u], g.N, c.cm, k, o, in.ok[u]);
                 }
             }
         };
@@ -514,6 +516,8 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         const auto& gr = in.gr;
         const auto& ok = in.ok;
         const auto& row = in.row;
+        constexpr bool BUF = kBufferStores<MODE, CPT, true>;
+        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
         float mu[RT], rs[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -561,7 +565,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     acc_b[e] += gv;
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
-                store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);
+                put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
             }
         }
     };
@@ -688,6 +692,8 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
         const auto& gr = in.gr;
         const auto& ok = in.ok;
         const auto& row = in.row;
+        constexpr bool BUF = kBufferStores<MODE, CPT, true>;
+        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
         float rs[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) rs[u] = in.rs[u];
@@ -728,7 +734,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     acc_w[e] += term;
                     o[v] = rs[u] * (gg - h * cc);
                 }
-                store_chunk<T, MODE, CPT>(dx, row[u], g.N, c.cm, k, o, ok[u]);
+                put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
             }
         }
     };
