@@ -82,6 +82,12 @@ struct ColMap {
     bool full[CPT];     // all V columns inside [0, N)
     bool any[CPT];      // at least one column inside [0, N)
     int shift;          // SHIFTED: s of this thread's rows
+    // SHIFTED only (fixed per thread, so computed once): the bits of each 32-bit word of chunk
+    // k that hold elements inside the row, and 1.0 / 0.0 per element inside / outside it.
+    // Kept as vector registers, they turn the per-element masks of the row loop into one AND
+    // per word and one multiply-add per element, with no per-element compares.
+    uint32_t keep[CPT][4];
+    float inrow[CPT][V];
 
     __device__ __forceinline__ void init(int lane, int tpr, int64_t N, int s, int chunk_base = 0) {
         shift = s;
@@ -92,6 +98,19 @@ struct ColMap {
             col0[k] = j0;
             full[k] = (j0 >= 0) && ((int64_t)j0 + V <= N);
             any[k] = ((int64_t)j0 + V > 0) && ((int64_t)j0 < N);
+            if constexpr (MODE == MODE_SHIFTED) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) keep[k][w] = 0u;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const bool in = j0 + v >= 0 && (int64_t)(j0 + v) < N;
+                    inrow[k][v] = in ? 1.f : 0.f;
+                    if (in) {
+                        if constexpr (sizeof(T) == 4) keep[k][v] = 0xFFFFFFFFu;
+                        else keep[k][v >> 1] |= (v & 1) ? 0xFFFF0000u : 0x0000FFFFu;
+                    }
+                }
+            }
         }
     }
     __device__ __forceinline__ bool valid(int k, int v, int64_t N) const {
@@ -218,13 +237,7 @@ __device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_
             u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(src.rsrc, off, 0, kNontemporal);
             if (MODE == MODE_SHIFTED) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const int j = cm.col0[k] + e;
-                    if (j < 0 || (int64_t)j >= N) {
-                        if constexpr (sizeof(T) == 4) v[e] = 0u;
-                        else v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-                    }
-                }
+                for (int w = 0; w < 4; ++w) v[w] &= cm.keep[k][w];
             }
             r.w[k][0] = v[0]; r.w[k][1] = v[1]; r.w[k][2] = v[2]; r.w[k][3] = v[3];
         }
@@ -351,10 +364,8 @@ __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int6
         }
     } else {
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const int j = cm.col0[k] + v;
-            if (j >= 0 && (int64_t)j < N) rp[v] = from_f32<T>(o[v]);
-        }
+        for (int v = 0; v < V; ++v)
+            if (cm.inrow[k][v] != 0.f) rp[v] = from_f32<T>(o[v]);
     }
 }
 

@@ -410,8 +410,14 @@ __device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
         for (int k = 0; k < CPT; ++k)
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const float d = xr[u].get(k, v) - mu[u];
-                a += cm.valid(k, v, g.N) ? d * d : 0.f;
+                if constexpr (MODE == MODE_SHIFTED) {
+                    // elements outside the row read as 0, so d is exactly 0 for them
+                    const float d = __builtin_fmaf(-mu[u], cm.inrow[k][v], xr[u].get(k, v));
+                    a = __builtin_fmaf(d, d, a);
+                } else {
+                    const float d = xr[u].get(k, v) - mu[u];
+                    a += cm.valid(k, v, g.N) ? d * d : 0.f;
+                }
             }
         s[u] = a;
     }
