@@ -445,9 +445,18 @@ constexpr int kMaxWaves = 16;
 // read is a memory load that would make the wave wait for all of its loads in flight.)
 template <int K>
 __device__ __forceinline__ void row_sum(float (&v)[K], int tpr, float* red, int& parity) {
-    const int g = tpr < 64 ? tpr : 64;
+    // The group size is uniform: one scalar branch picks a straight-line sum for it, instead
+    // of a branch around every step.
+    auto sums = [&](auto gc) {
 #pragma unroll
-    for (int i = 0; i < K; ++i) v[i] = group_sum(v[i], g);
+        for (int i = 0; i < K; ++i) v[i] = group_sum(v[i], decltype(gc)::value);
+    };
+    if (tpr >= 64) sums(IC<64>{});
+    else if (tpr == 32) sums(IC<32>{});
+    else if (tpr == 16) sums(IC<16>{});
+    else if (tpr == 8) sums(IC<8>{});
+    else if (tpr == 4) sums(IC<4>{});
+    else if (tpr == 2) sums(IC<2>{});
     if (tpr > 64) {
         const int wave = threadIdx.x >> 6;
         float* buf = red + parity * kMaxWaves * K;
