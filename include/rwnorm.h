@@ -20,8 +20,9 @@
  *            float32 [M].
  * Dtypes     x, dy, y, dx use x_dtype.  The parameters (alpha, gamma, beta, weight) and their
  *            gradients use param_dtype.  Supported pairs (x_dtype, param_dtype): (F32, F32),
- *            (BF16, F32), (BF16, BF16).  Arithmetic is float32; outputs are rounded once
- *            (round to nearest even) to their dtype, except for the RMSNorm rounding points.
+ *            (BF16, F32), (BF16, BF16), (F16, F32), (F16, F16).  Arithmetic is float32;
+ *            outputs are rounded once (round to nearest even; float16 overflows to +-inf) to
+ *            their dtype, except for the RMSNorm rounding points.
  * Ownership  Every pointer is device memory owned by the caller.  The library never allocates,
  *            frees or synchronizes on these calls; work is enqueued on `stream` (a hipStream_t,
  *            NULL = the default stream) and the call returns after launch.
@@ -36,10 +37,10 @@
  *            to run for the same inputs, device and library build.  A NULL gradient pointer
  *            skips writing that gradient.
  * Gradients  First-order only; eps is a constant.
- * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16
- *            elements) spread over at most 1024 threads; when N is not a multiple of the chunk
+ * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16 or
+ *            float16 elements) spread over at most 1024 threads; when N is not a multiple of the chunk
  *            or the operands are not 16-byte aligned a row may straddle one more chunk, so
- *            those LayerNorm/RMSNorm calls take N <= 16381 (float32) / 16377 (bfloat16) and
+ *            those LayerNorm/RMSNorm calls take N <= 16381 (float32) / 16377 (16-bit) and
  *            otherwise return RWN_ERR_UNSUPPORTED.  DyT splits wide rows into column blocks
  *            and takes every N up to 16384.
  */
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-typedef enum { RWN_F32 = 0, RWN_BF16 = 1 } rwn_dtype;
+typedef enum { RWN_F32 = 0, RWN_BF16 = 1, RWN_F16 = 2 } rwn_dtype;
 
 typedef enum {
     RWN_OK = 0,

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchma
 ``cpu_baseline`` leg are the only code that may import this package.  The GPU library never
 calls it and shares no code with it.
 
-Every function takes host tensors (torch CPU tensors of dtype float32 or bfloat16, row-major
+Every function takes host tensors (torch CPU tensors of dtype float32, bfloat16 or float16, row-major
 [M, N]) and returns a dict of float64 numpy arrays holding the exact values before the final
 cast to the output dtype, plus the per-element or per-column magnitude sums ("*_scale") that
 bound fp32 rounding error.  See ``oracle.c`` for the definition of each quantity and the
@@ -26,8 +26,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, F64 = 0, 1, 2
-_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64}
+F32, BF16, F64, F16 = 0, 1, 2, 3
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float64: F64, torch.float16: F16}
 
 
 def build(force: bool = True) -> str:
@@ -93,8 +93,12 @@ def _bind(lib):
     lib.oracle_round_bf16.restype = cd
     lib.oracle_round_f32.argtypes = [cd]
     lib.oracle_round_f32.restype = cd
+    lib.oracle_round_f16.argtypes = [cd]
+    lib.oracle_round_f16.restype = cd
     lib.oracle_round_array.argtypes = [dp, dp, i64, ci]
     lib.oracle_round_array.restype = None
+    lib.oracle_load_array.argtypes = [vp, ci, i64, dp]
+    lib.oracle_load_array.restype = None
     return lib
 
 
@@ -229,6 +233,22 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     out = np.empty_like(v)
     lib.oracle_round_array(v.ctypes.data, out.ctypes.data, v.size, BF16)
     return out
+
+
+def round_f16(v: np.ndarray) -> np.ndarray:
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    lib.oracle_round_array(v.ctypes.data, out.ctypes.data, v.size, F16)
+    return out
+
+
+def load_values(t: torch.Tensor) -> np.ndarray:
+    """The float64 values the oracle reads from a host tensor's elements."""
+    t = _host(t, "t")
+    out = np.empty(t.numel(), dtype=np.float64)
+    _load().oracle_load_array(t.data_ptr(), _DT[t.dtype], t.numel(), out.ctypes.data)
+    return out.reshape(tuple(t.shape))
 
 
 def round_f32(v: np.ndarray) -> np.ndarray:

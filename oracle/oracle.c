@@ -32,14 +32,17 @@
  *          derivative of RMSNorm is eps / (x^2 + eps)^(3/2).
  *
  * Dtype codes: 0 = float32, 1 = bfloat16 (stored as its 16 high bits of a float32),
- * 2 = float64 (no rounding at all; used by the finite-difference and library pins).
+ * 2 = float64 (no rounding at all; used by the finite-difference and library pins),
+ * 3 = float16 (IEEE 754 binary16: 1 sign, 5 exponent, 10 fraction bits).  The float16 pair
+ * follows the same reading as bfloat16 (the pages test bfloat16 and float16 alike): float32
+ * arithmetic, float16 storage and rounding points.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F64 = 2 };
+enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F64 = 2, ORA_F16 = 3 };
 
 /* Rows per block for column sums: each block sums its rows in row order, blocks are then
  * added in block order, so results do not depend on the OpenMP thread count. */
@@ -47,9 +50,21 @@ enum { ORA_F32 = 0, ORA_BF16 = 1, ORA_F64 = 2 };
 
 /* ---------------------------------------------------------------- element access / rounding */
 
+/* Exact value of a binary16 bit pattern: a zero exponent field holds subnormals f * 2^-24,
+ * the all-ones field infinities and NaNs, the rest (1024 + f) * 2^(e - 25). */
+static double f16_value(uint16_t h) {
+    const int e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
 static double load_elem(const void* p, int dt, int64_t i) {
     if (dt == ORA_F64) return ((const double*)p)[i];
     if (dt == ORA_F32) return (double)((const float*)p)[i];
+    if (dt == ORA_F16) return f16_value(((const uint16_t*)p)[i]);
     uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -73,8 +88,23 @@ double oracle_round_bf16(double v) {
 
 double oracle_round_f32(double v) { return (double)(float)v; }
 
+/* Round a double to the nearest float16 value, ties to even.  float16 has 11 significant bits
+ * and normal exponents down to -14, below which its spacing is fixed at 2^-24 (subnormals).
+ * The largest finite value is 65504; anything that rounds beyond it becomes +-inf. */
+double oracle_round_f16(double v) {
+    if (!isfinite(v) || v == 0.0) return v;
+    int e;
+    frexp(v, &e);                 /* |v| in [2^(e-1), 2^e) */
+    int q = e - 11;               /* spacing of 11-significant-bit numbers in that binade */
+    if (q < -24) q = -24;
+    double r = ldexp(nearbyint(ldexp(v, -q)), q);   /* nearbyint: ties to even (default mode) */
+    if (fabs(r) > 65504.0) r = copysign(INFINITY, v);
+    return r;
+}
+
 static double round_to(int dt, double v) {
     if (dt == ORA_F64) return v;
+    if (dt == ORA_F16) return oracle_round_f16(v);
     return dt == ORA_F32 ? oracle_round_f32(v) : oracle_round_bf16(v);
 }
 
@@ -290,22 +320,27 @@ typedef struct {
     double eps;
 } ln_ctx;
 
-/* Column terms of row i: [dy * xhat (N) | dy (N)]. */
+/* Column terms of row i: [dy * xhat (N) | dy (N) | |dy| * m (N)], where
+ * m = rstd * (|x| + mean_j |x_j|) is the magnitude of xhat's own terms (x and the mean). */
 static void ln_bwd_terms(const void* vctx, int64_t i, double* terms) {
     const ln_ctx* c = (const ln_ctx*)vctx;
     double mu, r;
     ln_row_stats(c->x, c->xdt, i, c->N, c->eps, &mu, &r);
+    const double am = row_abs_mean(c->x, c->xdt, i, c->N);
     for (int64_t j = 0; j < c->N; ++j) {
         double g = load_elem(c->dy, c->xdt, i * c->N + j);
-        terms[j] = g * (load_elem(c->x, c->xdt, i * c->N + j) - mu) * r;
+        double xv = load_elem(c->x, c->xdt, i * c->N + j);
+        terms[j] = g * (xv - mu) * r;
         terms[c->N + j] = g;
+        terms[2 * c->N + j] = fabs(g) * r * (fabs(xv) + am);
     }
 }
 
 /* [LN] backward, statistics recomputed from x in double (the GPU's saved stats are not read).
  * With g = dy * gamma, c1 = mean_j(g), c2 = mean_j(g * xhat):
  *   dx       = rstd * (g - c1 - xhat * c2)
- *   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij  (+ magnitude sums).
+ *   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij  (+ magnitude sums; dgamma's
+ *   expands xhat into its terms like dx_scale: sum_i |dy_ij| * m_ij, m as below).
  * dx_scale sums the magnitudes of every term of dx expanded through the row means:
  * with m = rstd * (|x| + mean_j |x_j|) (the magnitude of xhat's terms),
  * rstd * (|g| + mean_j |g_j| + m * mean_j |g_j| m_j). */
@@ -344,16 +379,16 @@ int oracle_layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, in
     }
     if (dgamma || dbeta || dgamma_scale || dbeta_scale) {
         ln_ctx c = {N, x, dy, xdt, eps};
-        double* s = (double*)malloc((size_t)(2 * N) * sizeof(double));
-        double* a = (double*)malloc((size_t)(2 * N) * sizeof(double));
-        if (!s || !a || column_sums(&c, ln_bwd_terms, M, 2 * N, s, a) != 0) {
+        double* s = (double*)malloc((size_t)(3 * N) * sizeof(double));
+        double* a = (double*)malloc((size_t)(3 * N) * sizeof(double));
+        if (!s || !a || column_sums(&c, ln_bwd_terms, M, 3 * N, s, a) != 0) {
             free(s); free(a);
             return -2;
         }
         for (int64_t j = 0; j < N; ++j) {
             if (dgamma) dgamma[j] = s[j];
             if (dbeta) dbeta[j] = s[N + j];
-            if (dgamma_scale) dgamma_scale[j] = a[j];
+            if (dgamma_scale) dgamma_scale[j] = a[2 * N + j];
             if (dbeta_scale) dbeta_scale[j] = a[N + j];
         }
         free(s); free(a);
@@ -378,7 +413,7 @@ static double rms_row_rstd(const void* x, int xdt, int64_t i, int64_t N, double 
  * carries a few float32 roundings) can land on either side.  Returns the other neighbour, or
  * n itself when h is not that close to a midpoint. */
 static double rounding_alternative(double h, double n, int dt) {
-    if (dt != ORA_BF16 || !isfinite(h) || h == n) return n;
+    if ((dt != ORA_BF16 && dt != ORA_F16) || !isfinite(h) || h == n) return n;
     double tol = ldexp(fabs(h), -18);
     double other = round_to(dt, 2.0 * h - n);   /* the neighbour on the other side of h */
     if (other == n) return n;
@@ -489,4 +524,9 @@ int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int 
 /* Exported for the pins: round an array of doubles to bfloat16 / float32 values. */
 void oracle_round_array(const double* in, double* out, int64_t n, int dt) {
     for (int64_t k = 0; k < n; ++k) out[k] = round_to(dt, in[k]);
+}
+
+/* The values the oracle reads from n stored elements of dtype dt. */
+void oracle_load_array(const void* p, int dt, int64_t n, double* out) {
+    for (int64_t k = 0; k < n; ++k) out[k] = load_elem(p, dt, k);
 }

@@ -19,7 +19,7 @@ __all__ = ["dyt_fwd", "dyt_bwd", "layernorm_fwd", "layernorm_bwd", "rmsnorm_fwd"
            "workspace_size", "version", "trace_begin", "trace_end", "copy_probe", "plan", "RwnError"]
 
 RwnError = _lib.RwnError
-_DT = {torch.float32: _lib.RWN_F32, torch.bfloat16: _lib.RWN_BF16}
+_DT = {torch.float32: _lib.RWN_F32, torch.bfloat16: _lib.RWN_BF16, torch.float16: _lib.RWN_F16}
 
 
 def _L():
@@ -28,7 +28,7 @@ def _L():
 
 def _dt(t: torch.Tensor, name: str) -> int:
     if t.dtype not in _DT:
-        raise TypeError(f"{name}: dtype {t.dtype} is not supported (float32 or bfloat16)")
+        raise TypeError(f"{name}: dtype {t.dtype} is not supported (float32, bfloat16 or float16)")
     return _DT[t.dtype]
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "librwnorm.so")
 HEADER = os.path.join(ROOT, "include", "rwnorm.h")
 
-RWN_F32, RWN_BF16 = 0, 1
+RWN_F32, RWN_BF16, RWN_F16 = 0, 1, 2
 STATUS = {0: "RWN_OK", 1: "RWN_ERR_INVALID_ARG", 2: "RWN_ERR_UNSUPPORTED", 3: "RWN_ERR_WORKSPACE",
           4: "RWN_ERR_LAUNCH"}
 KERNEL_TAGS = {1: "dyt_fwd", 2: "dyt_bwd", 3: "layernorm_fwd", 4: "layernorm_bwd", 5: "rmsnorm_fwd",

@@ -230,10 +230,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // the plan holds for every parameter dtype (the most restrictive kernel decides).
     int64_t occ = 0;
     if (occupancy) {
-        const int pdts[2] = {DT_F32, DT_BF16};
-        for (int i = 0; i < 2; ++i) {
+        const int pdts[3] = {DT_F32, DT_BF16, DT_F16};
+        for (int i = 0; i < 3; ++i) {
             if (pdt >= 0 && pdts[i] != pdt) continue;
-            if (xdt == DT_F32 && pdts[i] == DT_BF16) continue;   // no such pair
+            if (!dtype_pair_ok(xdt, pdts[i])) continue;
             const int n = resident_wgs(layer, backward, p, xdt, pdts[i]);
             if (n > 0) occ = occ == 0 ? n : std::min<int64_t>(occ, n);
         }
@@ -303,6 +303,9 @@ hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int
         if (pdt == DT_F32)
             return launch(colreduce_cm_kernel<float>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
                           (float*)out0, (float*)out1, (float*)out2);
+        if (pdt == DT_F16)
+            return launch(colreduce_cm_kernel<f16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+                          (f16_t*)out0, (f16_t*)out1, (f16_t*)out2);
         return launch(colreduce_cm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
                       (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
     }
@@ -319,6 +322,9 @@ hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int
     if (pdt == DT_F32) {
         return launch(colreduce_kernel<float>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
                       (float*)out0, (float*)out1, (float*)out2);
+    } else if (pdt == DT_F16) {
+        return launch(colreduce_kernel<f16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
+                      (f16_t*)out0, (f16_t*)out1, (f16_t*)out2);
     } else {
         return launch(colreduce_kernel<bf16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
                       (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);

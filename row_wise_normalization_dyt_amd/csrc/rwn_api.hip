@@ -61,12 +61,15 @@ rwn_status device_cus(int* cus) {
 rwn_status check_shape_dtypes(const char* fn, int64_t M, int64_t N, rwn_dtype xdt, rwn_dtype pdt) {
     if (M < 0) return fail(RWN_ERR_INVALID_ARG, "%s: M must be >= 0 (got %lld)", fn, (long long)M);
     if (N < 1) return fail(RWN_ERR_INVALID_ARG, "%s: N must be >= 1 (got %lld)", fn, (long long)N);
-    if ((int)xdt != RWN_F32 && (int)xdt != RWN_BF16)
+    if ((int)xdt != RWN_F32 && (int)xdt != RWN_BF16 && (int)xdt != RWN_F16)
         return fail(RWN_ERR_INVALID_ARG, "%s: unknown x dtype code %d", fn, (int)xdt);
-    if ((int)pdt != RWN_F32 && (int)pdt != RWN_BF16)
+    if ((int)pdt != RWN_F32 && (int)pdt != RWN_BF16 && (int)pdt != RWN_F16)
         return fail(RWN_ERR_INVALID_ARG, "%s: unknown parameter dtype code %d", fn, (int)pdt);
-    if (xdt == RWN_F32 && pdt == RWN_BF16)
-        return fail(RWN_ERR_UNSUPPORTED, "%s: float32 x with bfloat16 parameters is not supported", fn);
+    if (!dtype_pair_ok((int)xdt, (int)pdt)) {
+        static const char* names[3] = {"float32", "bfloat16", "float16"};
+        return fail(RWN_ERR_UNSUPPORTED, "%s: %s x with %s parameters is not supported", fn,
+                    names[(int)xdt], names[(int)pdt]);
+    }
     if (N > kMaxN)
         return fail(RWN_ERR_UNSUPPORTED, "%s: N = %lld is wider than the supported %lld", fn,
                     (long long)N, (long long)kMaxN);
@@ -455,10 +458,11 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
     if (misalign_bytes < 0 || misalign_bytes >= 16 || misalign_bytes % esz)
         return fail(RWN_ERR_INVALID_ARG, "%s: misalign_bytes must be a multiple of the element size below 16", fn);
     if (cus < 0) return fail(RWN_ERR_INVALID_ARG, "%s: cus must be >= 0", fn);
-    if (param_dtype != -1 && param_dtype != RWN_F32 && param_dtype != RWN_BF16)
-        return fail(RWN_ERR_INVALID_ARG, "%s: param_dtype must be -1, RWN_F32 or RWN_BF16", fn);
-    if (x_dtype == RWN_F32 && param_dtype == RWN_BF16)
-        return fail(RWN_ERR_UNSUPPORTED, "%s: float32 x with bfloat16 parameters is not supported", fn);
+    if (param_dtype != -1 && param_dtype != RWN_F32 && param_dtype != RWN_BF16 && param_dtype != RWN_F16)
+        return fail(RWN_ERR_INVALID_ARG, "%s: param_dtype must be -1, RWN_F32, RWN_BF16 or RWN_F16", fn);
+    if (param_dtype != -1 && !dtype_pair_ok((int)x_dtype, param_dtype))
+        return fail(RWN_ERR_UNSUPPORTED, "%s: x dtype %d with parameter dtype %d is not supported", fn,
+                    (int)x_dtype, param_dtype);
     const bool device = cus == 0;
     if (device && (st = device_cus(&cus)) != RWN_OK) return st;
     Plan p;

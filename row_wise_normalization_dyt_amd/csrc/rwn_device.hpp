@@ -28,15 +28,18 @@ namespace rwn {
 template <int V> using IC = std::integral_constant<int, V>;
 
 typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 enum Mode { MODE_ALIGNED = 0, MODE_SHIFTED = 1, MODE_SCALAR = 2 };
 
 template <typename T> struct ChunkOf;
 template <> struct ChunkOf<float> { static constexpr int value = 4; };
 template <> struct ChunkOf<bf16_t> { static constexpr int value = 8; };
+template <> struct ChunkOf<f16_t> { static constexpr int value = 8; };
 
 template <typename T, int MODE>
 struct Elems { static constexpr int value = (MODE == MODE_SCALAR) ? 1 : ChunkOf<T>::value; };
@@ -62,14 +65,29 @@ struct Geom {
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return (float)v; }
+__device__ __forceinline__ float to_f32(f16_t v) { return (float)v; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 // gfx950 lowers this to v_cvt_pk_bf16_f32: round to nearest even, NaN preserved.
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)v; }
+// v_cvt_f16_f32 under the default mode: round to nearest even, overflow to +-inf.
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float v) { return (f16_t)v; }
 
-// The float32 value of v after a round trip through storage dtype T.
+// float32 value of the 16-bit storage element held in the low half of `bits`.
+template <typename T> __device__ __forceinline__ float half_bits_to_f32(uint32_t bits) {
+    if constexpr (std::is_same<T, bf16_t>::value)
+        return __builtin_bit_cast(float, bits << 16);
+    else
+        return (float)__builtin_bit_cast(f16_t, (unsigned short)bits);
+}
+
+// The float32 value of v after a round trip through storage dtype T.  For float16 the float32
+// value is materialized first: otherwise the compiler may fuse the product that feeds it and
+// the conversion into one mixed-precision FMA (v_fma_mixlo_f16) that rounds once, straight to
+// float16, where a rounding point asks for the float32 product rounded to float16.
 template <typename T> __device__ __forceinline__ float round_through(float v) {
+    if constexpr (std::is_same<T, f16_t>::value) asm volatile("" : "+v"(v));
     return to_f32(from_f32<T>(v));
 }
 
@@ -134,9 +152,12 @@ struct RowRegs {
         if constexpr (sizeof(T) == 4) {
             return __builtin_bit_cast(float, w[k][MODE == MODE_SCALAR ? 0 : v]);
         } else {
-            if (MODE == MODE_SCALAR) return __builtin_bit_cast(float, w[k][0] << 16);
+            if (MODE == MODE_SCALAR) return half_bits_to_f32<T>(w[k][0]);
             const uint32_t u = w[k][v >> 1];
-            return __builtin_bit_cast(float, (v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+            if constexpr (std::is_same<T, bf16_t>::value)
+                return __builtin_bit_cast(float, (v & 1) ? (u & 0xFFFF0000u) : (u << 16));
+            else
+                return half_bits_to_f32<T>((v & 1) ? (u >> 16) : u);
         }
     }
 };
@@ -223,7 +244,6 @@ template <typename T, int MODE, int CPT>
 __device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_t N,
                                          const ColMap<T, MODE, CPT>& cm, bool rowvalid,
                                          RowRegs<T, MODE, CPT>& r) {
-    constexpr int V = RowRegs<T, MODE, CPT>::V;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const bool in = rowvalid && cm.any[k];
@@ -277,7 +297,10 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* o) {
                        __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3])};
     } else {
         f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-        return __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+        if constexpr (std::is_same<T, bf16_t>::value)
+            return __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+        else
+            return __builtin_bit_cast(u32x4, __builtin_convertvector(f, f16x8));
     }
 }
 
@@ -355,13 +378,7 @@ __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int6
     if constexpr (MODE == MODE_SCALAR) {
         *rp = from_f32<T>(o[0]);
     } else if (MODE == MODE_ALIGNED || cm.full[k]) {
-        if constexpr (sizeof(T) == 4) {
-            f32x4 v = {o[0], o[1], o[2], o[3]};
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(rp));
-        } else {
-            f32x8 f = {o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-            __builtin_nontemporal_store(__builtin_convertvector(f, bf16x8), reinterpret_cast<bf16x8*>(rp));
-        }
+        __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(rp));
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)

@@ -12,7 +12,14 @@
 namespace rwn {
 
 enum Layer { LAYER_DYT = 0, LAYER_LN = 1, LAYER_RMS = 2 };
-enum DType { DT_F32 = 0, DT_BF16 = 1 };
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// Supported (x dtype, parameter dtype) pairs: float32 x takes float32 parameters; a 16-bit x
+// takes float32 parameters or parameters of its own dtype.
+constexpr bool dtype_pair_ok(int xdt, int pdt) {
+    return (xdt == DT_F32 && pdt == DT_F32) || (xdt == DT_BF16 && (pdt == DT_F32 || pdt == DT_BF16)) ||
+           (xdt == DT_F16 && (pdt == DT_F32 || pdt == DT_F16));
+}
 
 // Widest row a plan covers: 16 waves x 64 lanes x 2 chunks (bf16) or x 4 chunks (f32).
 constexpr int64_t kMaxN = 16384;
@@ -90,6 +97,8 @@ hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
     if (xdt == DT_F32 && pdt == DT_F32) return f(TypeTag<float>{}, TypeTag<float>{});
     if (xdt == DT_BF16 && pdt == DT_F32) return f(TypeTag<bf16_t>{}, TypeTag<float>{});
     if (xdt == DT_BF16 && pdt == DT_BF16) return f(TypeTag<bf16_t>{}, TypeTag<bf16_t>{});
+    if (xdt == DT_F16 && pdt == DT_F32) return f(TypeTag<f16_t>{}, TypeTag<float>{});
+    if (xdt == DT_F16 && pdt == DT_F16) return f(TypeTag<f16_t>{}, TypeTag<f16_t>{});
     return hipErrorInvalidValue;
 }
 

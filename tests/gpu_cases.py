@@ -16,7 +16,7 @@ import row_wise_normalization_dyt_amd as rwn
 from tests import tolerance as tol
 import workloads
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def gpu_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, use_stats: bool = True) -> Dict[str, torch.Tensor]:

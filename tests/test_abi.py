@@ -56,6 +56,11 @@ def test_dtype_errors(lib):
     assert lib.dyt_fwd(4, 8, P, 0, P, P, P, 9, P, None) == 1
     assert lib.rmsnorm_fwd(4, 8, P, 0, P, 1, 1e-6, P, None, None) == 2     # f32 x, bf16 weight
     assert "not supported" in _err(lib)
+    assert lib.rmsnorm_fwd(4, 8, P, 0, P, 2, 1e-6, P, None, None) == 2     # f32 x, f16 weight
+    assert lib.dyt_fwd(4, 8, P, 1, P, P, P, 2, P, None) == 2               # bf16 x, f16 params
+    assert lib.dyt_fwd(4, 8, P, 2, P, P, P, 1, P, None) == 2               # f16 x, bf16 params
+    assert "float16 x with bfloat16 parameters" in _err(lib)
+    assert lib.dyt_fwd(4, 8, P, 3, P, P, P, 0, P, None) == 1               # no dtype code 3
 
 
 def test_null_and_eps_errors(lib):
@@ -108,7 +113,7 @@ SHAPES = [(1, 1), (7, 24), (4096, 64), (401408, 24), (1048573, 32), (1048573, 12
           (3, 7), (257, 17), (7, 129), (4099, 130), (7, 2049), (65537, 255), (5, 1023)]
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("backward", [False, True])
 @pytest.mark.parametrize("M,N", SHAPES)
 def test_plan_covers_rows_and_columns(M, N, dtype, backward):

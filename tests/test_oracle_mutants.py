@@ -30,8 +30,7 @@ MUTANTS = [
     ("ln_eps_outside_sqrt", "*rstd_out = 1.0 / sqrt(v + eps);", "*rstd_out = 1.0 / (sqrt(v) + eps);"),
     ("ln_dx_sign", "if (dx) dx[i * N + j] = r * (g - c1 - xh * c2);", "if (dx) dx[i * N + j] = r * (g - c1 + xh * c2);"),
     ("ln_c1_uses_dy", "                c1 += g;\n", "                c1 += load_elem(dy, xdt, i * N + j);\n"),
-    ("ln_dgamma_drops_rstd", "terms[j] = g * (load_elem(c->x, c->xdt, i * c->N + j) - mu) * r;",
-     "terms[j] = g * (load_elem(c->x, c->xdt, i * c->N + j) - mu);"),
+    ("ln_dgamma_drops_rstd", "terms[j] = g * (xv - mu) * r;", "terms[j] = g * (xv - mu);"),
     ("rms_n_not_rounded", "            double n = round_to(xdt, h);\n", "            double n = h;\n"),
     ("rms_g_not_rounded", "double g = round_to(xdt, round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j)));\n                double h",
      "double g = round_arith(xdt, load_elem(dy, xdt, i * N + j) * load_elem(w, wdt, j));\n                double h"),
@@ -43,6 +42,11 @@ MUTANTS = [
      "int64_t i1 = ((b + 1) * ORA_ROW_BLOCK < M ? (b + 1) * ORA_ROW_BLOCK : M) - 1;"),
     ("bf16_ties_away", "double r = ldexp(nearbyint(ldexp(v, -q)), q);", "double r = ldexp(round(ldexp(v, -q)), q);"),
     ("bf16_seven_bits", "int q = e - 8;", "int q = e - 7;"),
+    ("f16_nine_fraction_bits", "int q = e - 11;", "int q = e - 10;"),
+    ("f16_subnormal_spacing", "if (q < -24) q = -24;", "if (q < -25) q = -25;"),
+    ("f16_no_overflow", "if (fabs(r) > 65504.0) r = copysign(INFINITY, v);", ""),
+    ("f16_exponent_bias", "else v = ldexp((double)(1024 + f), e - 25);", "else v = ldexp((double)(1024 + f), e - 24);"),
+    ("f16_subnormal_read", "if (e == 0) v = ldexp((double)f, -24);", "if (e == 0) v = ldexp((double)(1024 + f), -25);"),
 ]
 
 

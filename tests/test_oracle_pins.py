@@ -56,6 +56,83 @@ def test_round_bf16_rounds_doubles_directly_not_through_float32():
     assert oracle.round_bf16(np.array([2.0 ** 128]))[0] == np.inf
 
 
+# ------------------------------------------------------------------------- float16 values
+
+def _all_f16():
+    return torch.arange(0, 2 ** 16, dtype=torch.int32).to(torch.int16).view(torch.float16)
+
+
+def test_f16_values_read_exactly():
+    """Every binary16 bit pattern reads as the value torch's exact float16 -> float64
+    conversion gives (subnormals, infinities and NaNs included)."""
+    h = _all_f16()
+    got = oracle.load_values(h)
+    expect = h.to(torch.float64).numpy()
+    nan = np.isnan(expect)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], expect[~nan])
+
+
+def _f16_nearest_brute_force(vals):
+    """Round to nearest float16, ties to the even bit pattern, by search over every finite
+    float16 value; beyond 65504 the next step (65536) stands for infinity."""
+    h = _all_f16()
+    v = h.to(torch.float64).numpy()
+    bits = h.view(torch.int16).numpy().astype(np.int64) & 0xFFFF
+    fin = np.isfinite(v) & (bits < 0x8000)            # non-negative finite values, ascending
+    mags, mbits = v[fin], bits[fin]
+    order = np.argsort(mags, kind="stable")
+    mags, mbits = mags[order], mbits[order]
+    mags = np.append(mags, 65536.0)
+    mbits = np.append(mbits, 0x7C00)
+    out = []
+    for x in vals:
+        a = abs(x)
+        k = int(np.searchsorted(mags, a, side="left"))
+        if k == len(mags):
+            r = 65536.0
+        elif mags[k] == a:
+            r = mags[k]
+        else:
+            lo, hi = mags[k - 1], mags[k]
+            dlo, dhi = a - lo, hi - a
+            if dlo < dhi or (dlo == dhi and mbits[k - 1] % 2 == 0):
+                r = lo
+            else:
+                r = hi
+        r = np.inf if r == 65536.0 else r
+        out.append(math.copysign(r, x))
+    return np.array(out)
+
+
+def test_round_f16_against_brute_force_nearest():
+    """Exact ties (midpoints of neighbouring float16 values), values one double ulp either side
+    of them, the subnormal range, the overflow threshold and log-uniform random doubles."""
+    h = _all_f16().to(torch.float64).numpy()
+    pos = np.unique(h[np.isfinite(h) & (h >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2                     # exact in float64
+    rng = np.random.default_rng(5)
+    pick = rng.choice(len(mids), size=3000, replace=False)
+    m = mids[pick]
+    rand = np.exp2(rng.uniform(-30, 17, size=3000)) * rng.choice([-1.0, 1.0], size=3000)
+    special = np.array([65504.0, 65519.99, 65520.0, 65520.0 - 2 ** -20, 2.0 ** -24, 2.0 ** -25,
+                        3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1e9, -1e9])
+    vals = np.concatenate([m, np.nextafter(m, 0), np.nextafter(m, np.inf), -m, rand, special])
+    got = oracle.round_f16(vals)
+    assert np.array_equal(got, _f16_nearest_brute_force(vals))
+
+
+def test_round_f16_matches_torch_on_float32_values():
+    """On float32 inputs the rounding agrees with torch's float32 -> float16 cast."""
+    rng = np.random.default_rng(6)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    expect = torch.from_numpy(vals.copy()).to(torch.float16).to(torch.float64).numpy()
+    got = oracle.round_f16(vals.astype(np.float64))
+    assert np.array_equal(got, expect)
+
+
 # ---------------------------------------------------------------------------- DyT pins
 
 def _tanh_cases():
@@ -345,6 +422,38 @@ def test_rmsnorm_bf16_matches_eager_expression():
     ora_dw = oracle.round_bf16(bw["dweight"])
     eager_dw = w.grad.double().numpy()
     ulpw = np.exp2(np.floor(np.log2(np.abs(eager_dw))) - 7)
+    assert np.all(np.abs(ora_dw - eager_dw) <= 2 * ulpw)
+
+
+def test_rmsnorm_f16_matches_eager_expression():
+    """The same eager expression in float16 (float32 statistics, float16 rounding points)
+    against the oracle: as for bfloat16, only rare one-step differences in y where float32 and
+    float64 statistics straddle a float16 rounding boundary."""
+    M, N = 64, 96
+    xh = _randn((M, N), 91, torch.float32).to(torch.float16)
+    wh = _randn(N, 92, torch.float32, scale=0.02, shift=1.0).to(torch.float16)
+    dyh = _randn((M, N), 93, torch.float32).to(torch.float16)
+    eps = 1e-6
+    x = xh.clone().requires_grad_(True)
+    w = wh.clone().requires_grad_(True)
+    xf = x.float()
+    y = w * (xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)).to(x.dtype)
+    y.backward(dyh)
+    fw = oracle.rmsnorm_fwd(xh, wh, float(np.float32(eps)))
+    ora_y = oracle.round_f16(fw["y"])
+    eager_y = y.detach().double().numpy()
+    assert (ora_y == eager_y).mean() >= 0.99
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.abs(eager_y) + 1e-30)), -14) - 10)
+    assert np.all(np.abs(ora_y - eager_y) <= ulp * 1.0001)
+    bw = oracle.rmsnorm_bwd(xh, dyh, wh, float(np.float32(eps)))
+    ora_dx = oracle.round_f16(bw["dx"])
+    eager_dx = x.grad.double().numpy()
+    assert (ora_dx == eager_dx).mean() >= 0.9
+    ulpx = np.exp2(np.maximum(np.floor(np.log2(np.abs(eager_dx) + 1e-30)), -14) - 10)
+    assert np.all(np.abs(ora_dx - eager_dx) <= 4 * ulpx + 1e-6 * bw["dx_scale"])
+    ora_dw = oracle.round_f16(bw["dweight"])
+    eager_dw = w.grad.double().numpy()
+    ulpw = np.exp2(np.floor(np.log2(np.abs(eager_dw))) - 10)
     assert np.all(np.abs(ora_dw - eager_dw) <= 2 * ulpw)
 
 

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path against the CPU oracle, element by element (needs an MI355X).
 
 Bars (tests/tolerance.py): float32 y/dx within 1e-5 of the magnitude sum of their terms;
-bfloat16 y/dx within one bf16 ulp plus that; parameter gradients within 1e-4 of the column's
+bfloat16/float16 y/dx within one ulp of the dtype plus that; parameter gradients within 1e-4 of the column's
 sum of |terms| plus one ulp of the parameter dtype; NaN/Inf only where the oracle has them.
 Parameter gradients must also be bitwise identical from run to run.
 """
@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import row_wise_normalization_dyt_amd as rwn
 import workloads
 from tests import gpu_cases as gc
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 LAYERS = ("dyt", "layernorm", "rmsnorm")
-DTYPE_PAIRS = (("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"))
+DTYPE_PAIRS = (("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f32"), ("f16", "f16"))
 
 
 def _banner(*a):
@@ -96,13 +97,14 @@ def test_layernorm_without_affine():
     tol.assert_reports(gc.check_workload(wl, DEV, inputs=inp))
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f16"])
 @pytest.mark.parametrize("layer", LAYERS)
 @pytest.mark.parametrize("offset", [1, 3])
-def test_misaligned_operands_take_the_shifted_path(layer, offset):
-    """x and dy are views starting `offset` bf16 elements past a 16-byte boundary."""
+def test_misaligned_operands_take_the_shifted_path(layer, offset, xdt):
+    """x and dy are views starting `offset` 16-bit elements past a 16-byte boundary."""
     reps = []
     for (M, N) in [(513, 1025), (100, 999), (37, 129), (65, 24)]:
-        wl = workloads.small(layer, M, N, "bf16", "f32", seed=M + offset)
+        wl = workloads.small(layer, M, N, xdt, "f32", seed=M + offset)
         _banner(wl, "offset", offset)
         inp = workloads.make_inputs(wl)
         dev = {}
@@ -117,8 +119,41 @@ def test_misaligned_operands_take_the_shifted_path(layer, offset):
                 dev[k] = v.to(DEV)
         g = gc.gpu_run(layer, dev, wl.eps)
         o = gc.oracle_run(layer, inp, wl.eps)
-        reps += gc.compare(layer, g, o, torch.bfloat16, torch.float32)
+        reps += gc.compare(layer, g, o, gc.DT[xdt], torch.float32)
     tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("layer", LAYERS)
+def test_float16_outputs_overflow_to_infinity(layer):
+    """float16 tops out at 65504: outputs whose exact value rounds beyond it are +-inf, and
+    every other element stays within the usual bound (the oracle's exact values rounded to
+    float16 decide which elements overflow)."""
+    M, N = 257, 136
+    wl = workloads.small(layer, M, N, "f16", "f32", seed=5)
+    _banner(wl, "overflow")
+    inp = workloads.make_inputs(wl)
+    big = torch.linspace(30000.0, 70000.0, N)
+    if layer == "rmsnorm":
+        inp["weight"] = big.to(torch.float32)
+    else:
+        inp["gamma"] = big.to(torch.float32)
+        inp["beta"] = (big / 2).to(torch.float32)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    g = gc.gpu_run(layer, dev, wl.eps)
+    torch.cuda.synchronize()
+    o = gc.oracle_run(layer, inp, wl.eps, grads=False)
+    ry = oracle.round_f16(o["y"])
+    gy = g["y"].double().cpu().numpy()
+    # Within float32 rounding of the threshold 65520 either side is a correct result.
+    edge = np.abs(np.abs(o["y"]) - 65520.0) <= 1e-4 * 65520.0
+    over = np.isinf(ry) & ~edge
+    fin = ~np.isinf(ry) & ~edge
+    assert over.any() and fin.any()
+    assert np.array_equal(gy[over], ry[over])
+    mask = torch.as_tensor(fin, device=g["y"].device)
+    r = tol.compare(f"{layer}.y", g["y"][mask], o["y"][fin], o["y_scale"][fin],
+                    torch.float16, alt=None if o.get("y_alt") is None else o["y_alt"][fin])
+    tol.assert_reports([r])
 
 
 def test_non_contiguous_and_batched_inputs():

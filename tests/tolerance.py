@@ -2,7 +2,8 @@
 
 Bounds (the oracle returns the exact value before the final cast plus a magnitude sum S):
   float32 outputs and dx:      |gpu - exact| <= 1e-5 * S_e                    (+ a 4*FLT_MIN floor)
-  bfloat16 outputs and dx:     |gpu - exact| <= ulp_bf16 + 1e-5 * S_e         (1 bf16 ulp after fp32 compute)
+  bfloat16 / float16 outputs and dx:
+                               |gpu - exact| <= ulp + 1e-5 * S_e              (1 ulp of the dtype after fp32 compute)
   parameter gradients:         |gpu - exact| <= 1e-4 * sum_i |term_ij| + ulp_param_dtype
                                (+ RMSNorm: the summed change of terms whose normalized value
                                has two admissible roundings)
@@ -26,9 +27,9 @@ REL_PARAM = 1e-4
 def ulp(v: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     """Spacing of dtype's values at |v| (binade-based; subnormal spacing below the normal range)."""
     a = np.abs(np.asarray(v, dtype=np.float64))
-    mant = 7 if dtype == torch.bfloat16 else 23
+    mant, emin = {torch.bfloat16: (7, -126), torch.float16: (10, -14)}.get(dtype, (23, -126))
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(e, -126)
+    e = np.maximum(e, emin)
     return np.where(np.isfinite(a), np.exp2(e - mant), np.inf)
 
 
@@ -58,7 +59,7 @@ def compare(name: str, gpu: torch.Tensor, exact: np.ndarray, scale: np.ndarray, 
     if alt is not None:
         err = np.minimum(err, np.abs(g - np.asarray(alt, dtype=np.float64)))
     u = ulp(np.maximum(np.abs(g), np.abs(ex)), out_dtype)
-    if out_dtype == torch.bfloat16:
+    if out_dtype in (torch.bfloat16, torch.float16):
         bound = u + rel * np.asarray(scale, dtype=np.float64)
     else:
         bound = rel * np.asarray(scale, dtype=np.float64) + 4 * FLT_MIN

@@ -32,7 +32,7 @@ import torch
 BASE_SEED = 20261202
 
 LAYERS = ("dyt", "layernorm", "rmsnorm")
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -43,7 +43,7 @@ class Workload:
     layer: str
     M: int
     N: int
-    xdt: str                      # "f32" | "bf16"
+    xdt: str                      # "f32" | "bf16" | "f16"
     pdt: str                      # dtype of alpha/gamma/beta or of the RMSNorm weight
     seed: int
     x_std: float = 1.0
@@ -153,7 +153,7 @@ def make_inputs(wl: Workload, device="cpu", seed_offset: int = 0) -> Dict[str, t
     if wl.layer == "dyt" and math.isinf(wl.alpha):
         # With alpha = +inf an exact zero is a true NaN (tanh(inf * 0)); the generators can emit
         # 0.0 (about once per 2^24 draws), so such elements are moved to the smallest normal.
-        tiny = torch.finfo(torch.float32).tiny
+        tiny = torch.finfo(xdt).tiny
         x = torch.where(x == 0, torch.full_like(x, tiny), x)
     out = {"x": x}
     del x
