@@ -112,6 +112,13 @@ def standard_workloads() -> Dict[str, Workload]:
             w[f"wide_{layer}_bf16_65536x{n}"] = Workload(
                 f"wide_{layer}_bf16_65536x{n}", layer, 65536, n, "bf16", "f32", _cfg_seed(5),
                 gamma_mean=1.0, gamma_std=0.1, beta_mean=1.0, beta_std=0.1, alpha=0.5, eps=eps)
+    # float16 counterparts of one shape from each of configurations 3, 4 and 5 (same seeds and
+    # value distributions; float16 activations, parameters as in the bfloat16 originals but in
+    # float16 where those were bfloat16).
+    for base, pdt in (("dyt_bf16_1048573x128", "f32"), ("rmsnorm_bf16_16384x2048", "f16"),
+                      ("wide_layernorm_bf16_65536x4096", "f32")):
+        name = base.replace("bf16", "f16")
+        w[name] = dataclasses.replace(w[base], name=name, xdt="f16", pdt=pdt)
     return w
 
 
