@@ -82,7 +82,7 @@ def time_workload(wl, steps: int, warmup: int, trace: bool = True):
     sets = []
     for i in range(nsets):
         inp = base if i == 0 else {k: v.clone() for k, v in base.items()}
-        sets.append(PreparedStep(wl.layer, inp, wl.eps))
+        sets.append(PreparedStep(wl.layer, inp, wl.eps, form=wl.form))
     for i in range(warmup):
         sets[i % nsets].step()
     torch.cuda.synchronize()
@@ -140,8 +140,8 @@ def cpu_baseline(wl, inputs, target_s: float):
             oracle.layernorm_fwd(sub["x"], sub["gamma"], sub["beta"], e)
             oracle.layernorm_bwd(sub["x"], sub["dy"], sub["gamma"], e)
         else:
-            oracle.rmsnorm_fwd(sub["x"], sub["weight"], e)
-            oracle.rmsnorm_bwd(sub["x"], sub["dy"], sub["weight"], e)
+            oracle.rmsnorm_fwd(sub["x"], sub["weight"], e, form=wl.form)
+            oracle.rmsnorm_bwd(sub["x"], sub["dy"], sub["weight"], e, form=wl.form)
         return time.perf_counter() - t
 
     S0 = max(1, min(wl.M, 2_000_000 // wl.N))

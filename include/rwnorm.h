@@ -132,6 +132,32 @@ rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, rwn_
 
 rwn_status rmsnorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes);
 
+/* RMSNorm forms.  The same passage (DeepSpeed PR #8645, "Which modules are replaced" and "Not
+ * covered") names two forms besides the Llama one whose math differs only in where the weight
+ * meets the rounding: classes that multiply by the weight before the cast to x's dtype, and
+ * the Gemma family's (1 + weight).  Both multiply in float32 and round once:
+ *   RWN_RMS_CAST_THEN_WEIGHT  y = weight * (x * rstd).to(x.dtype)        (rmsnorm_fwd above)
+ *   RWN_RMS_WEIGHT_THEN_CAST  y = (weight * (x * rstd)).to(x.dtype)
+ *   RWN_RMS_ONE_PLUS_WEIGHT   y = ((1 + weight) * (x * rstd)).to(x.dtype), 1 + weight in float32
+ * Backward of the two float32 forms, with s = weight or (1 + weight) and h = x * rstd:
+ *   g = dy * s (float32, not rounded), c = mean_j g * h, dx = rstd * (g - h * c),
+ *   dweight_j = sum_i dy * h in float32, rounded once to the weight's dtype. */
+typedef enum {
+    RWN_RMS_CAST_THEN_WEIGHT = 0,
+    RWN_RMS_WEIGHT_THEN_CAST = 1,
+    RWN_RMS_ONE_PLUS_WEIGHT = 2
+} rwn_rms_form;
+
+/* rmsnorm_fwd / rmsnorm_bwd for any form; the other arguments and rules are theirs.  An unknown
+ * form returns RWN_ERR_INVALID_ARG. */
+rwn_status rmsnorm_fwd_form(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                            const void* weight, rwn_dtype weight_dtype, float eps, rwn_rms_form form,
+                            void* y, float* rstd, void* stream);
+rwn_status rmsnorm_bwd_form(int64_t M, int64_t N, const void* x, const void* dy, rwn_dtype x_dtype,
+                            const float* rstd, const void* weight, rwn_dtype weight_dtype, float eps,
+                            rwn_rms_form form, void* dx, void* dweight, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------ support */
 
 /* Message of the last failed call on this thread ("" after a successful call). */

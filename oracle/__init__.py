@@ -86,8 +86,10 @@ def _bind(lib):
     lib.oracle_layernorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp, dp]
     lib.oracle_rmsnorm_fwd.argtypes = [i64, i64, vp, ci, vp, ci, cd, dp, dp, dp, dp]
     lib.oracle_rmsnorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_fwd_form.argtypes = [i64, i64, vp, ci, vp, ci, cd, ci, dp, dp, dp, dp]
+    lib.oracle_rmsnorm_bwd_form.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, ci, dp, dp, dp, dp, dp]
     for f in ("oracle_dyt_fwd", "oracle_dyt_bwd", "oracle_layernorm_fwd", "oracle_layernorm_bwd",
-              "oracle_rmsnorm_fwd", "oracle_rmsnorm_bwd"):
+              "oracle_rmsnorm_fwd", "oracle_rmsnorm_bwd", "oracle_rmsnorm_fwd_form", "oracle_rmsnorm_bwd_form"):
         getattr(lib, f).restype = ci
     lib.oracle_round_bf16.argtypes = [cd]
     lib.oracle_round_bf16.restype = cd
@@ -200,27 +202,31 @@ def layernorm_bwd(x, dy, gamma, eps: float, want_dx: bool = True) -> Dict[str, n
     return out
 
 
-def rmsnorm_fwd(x, weight, eps: float) -> Dict[str, np.ndarray]:
+RMS_FORMS = {"cast_then_weight": 0, "weight_then_cast": 1, "one_plus_weight": 2}
+
+
+def rmsnorm_fwd(x, weight, eps: float, form: str = "cast_then_weight") -> Dict[str, np.ndarray]:
     lib = _load()
     x, weight = _host(x, "x"), _host(weight, "weight")
     M, N = x.shape
     y, ys, ya, rs = _out((M, N)), _out((M, N)), _out((M, N)), _out(M)
-    _check(lib.oracle_rmsnorm_fwd(M, N, x.data_ptr(), _DT[x.dtype], weight.data_ptr(),
-                                  _DT[weight.dtype], float(eps), _p(y), _p(ys), _p(ya), _p(rs)),
-           "oracle_rmsnorm_fwd")
+    _check(lib.oracle_rmsnorm_fwd_form(M, N, x.data_ptr(), _DT[x.dtype], weight.data_ptr(),
+                                       _DT[weight.dtype], float(eps), RMS_FORMS[form], _p(y), _p(ys),
+                                       _p(ya), _p(rs)), "oracle_rmsnorm_fwd_form")
     return {"y": y, "y_scale": ys, "y_alt": ya, "rstd": rs}
 
 
-def rmsnorm_bwd(x, dy, weight, eps: float, want_dx: bool = True) -> Dict[str, np.ndarray]:
+def rmsnorm_bwd(x, dy, weight, eps: float, want_dx: bool = True,
+                form: str = "cast_then_weight") -> Dict[str, np.ndarray]:
     lib = _load()
     x, dy, weight = _host(x, "x"), _host(dy, "dy"), _host(weight, "weight")
     M, N = x.shape
     dx = _out((M, N)) if want_dx else None
     dxs = _out((M, N)) if want_dx else None
     dw, dws, dwl = _out(N), _out(N), _out(N)
-    _check(lib.oracle_rmsnorm_bwd(M, N, x.data_ptr(), dy.data_ptr(), _DT[x.dtype],
-                                  weight.data_ptr(), _DT[weight.dtype], float(eps), _p(dx), _p(dxs),
-                                  _p(dw), _p(dws), _p(dwl)), "oracle_rmsnorm_bwd")
+    _check(lib.oracle_rmsnorm_bwd_form(M, N, x.data_ptr(), dy.data_ptr(), _DT[x.dtype],
+                                       weight.data_ptr(), _DT[weight.dtype], float(eps), RMS_FORMS[form],
+                                       _p(dx), _p(dxs), _p(dw), _p(dws), _p(dwl)), "oracle_rmsnorm_bwd_form")
     out = {"dweight": dw, "dweight_scale": dws, "dweight_slack": dwl}
     if want_dx:
         out.update(dx=dx, dx_scale=dxs)

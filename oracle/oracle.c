@@ -521,6 +521,94 @@ int oracle_rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, int 
     return 0;
 }
 
+/* The two float32 forms of the same passage ([RMS] "Which modules are replaced" and "Not
+ * covered"): classes that multiply by the weight before the cast, and the (1 + weight) family.
+ * Both scale the unrounded normalized value h = x * r in float32 and round once:
+ * y = s_j * h with s_j = w_j (form 1) or s_j = round_arith(1 + w_j) (form 2; eager adds 1 to
+ * the float32 weight).  The final cast is left to the caller's tolerance; y_scale = |y|; there
+ * is no alternative rounding (y_alt = y).  Form 0 is the Llama form above. */
+static double rms_form_scale(int form, int xdt, double wj) {
+    return form == 2 ? round_arith(xdt, 1.0 + wj) : wj;
+}
+
+int oracle_rmsnorm_fwd_form(int64_t M, int64_t N, const void* x, int xdt, const void* w, int wdt,
+                            double eps, int form, double* y, double* y_scale, double* y_alt,
+                            double* rstd) {
+    if (form == 0) return oracle_rmsnorm_fwd(M, N, x, xdt, w, wdt, eps, y, y_scale, y_alt, rstd);
+    if ((form != 1 && form != 2) || M < 0 || N < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double r = rms_row_rstd(x, xdt, i, N, eps);
+        if (rstd) rstd[i] = r;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = rms_form_scale(form, xdt, load_elem(w, wdt, j)) * (load_elem(x, xdt, i * N + j) * r);
+            if (y) y[i * N + j] = v;
+            if (y_scale) y_scale[i * N + j] = fabs(v);
+            if (y_alt) y_alt[i * N + j] = v;
+        }
+    }
+    return 0;
+}
+
+/* Column terms of row i for the float32 forms: dy * h (unrounded; the weight gradient of a
+ * float32 product is summed in float32 and rounded once), and no slack. */
+static void rms_form_bwd_terms(const void* vctx, int64_t i, double* terms) {
+    const rms_ctx* c = (const rms_ctx*)vctx;
+    double r = rms_row_rstd(c->x, c->xdt, i, c->N, c->eps);
+    for (int64_t j = 0; j < c->N; ++j) {
+        terms[j] = load_elem(c->dy, c->xdt, i * c->N + j) * (load_elem(c->x, c->xdt, i * c->N + j) * r);
+        terms[c->N + j] = 0.0;
+    }
+}
+
+/* Backward of the float32 forms: g = dy * s_j (no rounding: the product stays in float32);
+ * h = x * r; c = mean_j(g * h); dx = r * (g - h * c), dx_scale as in the Llama form;
+ * dw_j = sum_i dy_ij * h_ij (+ magnitude sum; dw_slack = 0). */
+int oracle_rmsnorm_bwd_form(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
+                            const void* w, int wdt, double eps, int form, double* dx,
+                            double* dx_scale, double* dw, double* dw_scale, double* dw_slack) {
+    if (form == 0)
+        return oracle_rmsnorm_bwd(M, N, x, dy, xdt, w, wdt, eps, dx, dx_scale, dw, dw_scale, dw_slack);
+    if ((form != 1 && form != 2) || M < 0 || N < 1) return -1;
+    if (dx || dx_scale) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < M; ++i) {
+            double r = rms_row_rstd(x, xdt, i, N, eps);
+            double c = 0.0, a = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                double g = load_elem(dy, xdt, i * N + j) * rms_form_scale(form, xdt, load_elem(w, wdt, j));
+                double h = load_elem(x, xdt, i * N + j) * r;
+                c += g * h;
+                a += fabs(g * h);
+            }
+            c /= (double)N;
+            a /= (double)N;
+            for (int64_t j = 0; j < N; ++j) {
+                double g = load_elem(dy, xdt, i * N + j) * rms_form_scale(form, xdt, load_elem(w, wdt, j));
+                double h = load_elem(x, xdt, i * N + j) * r;
+                if (dx) dx[i * N + j] = r * (g - h * c);
+                if (dx_scale) dx_scale[i * N + j] = r * (fabs(g) + fabs(h) * a);
+            }
+        }
+    }
+    if (dw || dw_scale || dw_slack) {
+        rms_ctx c = {N, x, dy, xdt, wdt, eps};
+        double* s = (double*)malloc((size_t)(2 * N) * sizeof(double));
+        double* a = (double*)malloc((size_t)(2 * N) * sizeof(double));
+        if (!s || !a || column_sums(&c, rms_form_bwd_terms, M, 2 * N, s, a) != 0) {
+            free(s); free(a);
+            return -2;
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            if (dw) dw[j] = s[j];
+            if (dw_scale) dw_scale[j] = a[j];
+            if (dw_slack) dw_slack[j] = 0.0;
+        }
+        free(s); free(a);
+    }
+    return 0;
+}
+
 /* Exported for the pins: round an array of doubles to bfloat16 / float32 values. */
 void oracle_round_array(const double* in, double* out, int64_t n, int dt) {
     for (int64_t k = 0; k < n; ++k) out[k] = round_to(dt, in[k]);

@@ -196,8 +196,19 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
 
 # -------------------------------------------------------------------------------- RMSNorm
 
-def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: bool = True):
-    """Returns (y, rstd [M] float32 or None); y keeps x's dtype."""
+RMS_FORMS = {"cast_then_weight": 0, "weight_then_cast": 1, "one_plus_weight": 2}
+
+
+def _form(form: str) -> int:
+    if form not in RMS_FORMS:
+        raise ValueError(f"unknown RMSNorm form {form!r} (one of {sorted(RMS_FORMS)})")
+    return RMS_FORMS[form]
+
+
+def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: bool = True,
+                form: str = "cast_then_weight"):
+    """Returns (y, rstd [M] float32 or None); y keeps x's dtype.  form: "cast_then_weight"
+    (Llama), "weight_then_cast" or "one_plus_weight" (Gemma)."""
     lib = _L()
     x2 = _as_2d(x, "x")
     M, N = x2.shape
@@ -205,14 +216,14 @@ def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: b
     y = _like(x2)
     rstd = torch.empty(M, dtype=torch.float32, device=x2.device) if want_stats else None
     with torch.cuda.device(x2.device):
-        _lib.check(lib, "rmsnorm_fwd", lib.rmsnorm_fwd(M, N, _ptr(x2), _dt(x2, "x"), _ptr(weight),
-                                                       _dt(weight, "weight"), float(eps), _ptr(y), _ptr(rstd),
-                                                       _stream(x2.device)))
+        _lib.check(lib, "rmsnorm_fwd_form", lib.rmsnorm_fwd_form(M, N, _ptr(x2), _dt(x2, "x"), _ptr(weight),
+                                                                 _dt(weight, "weight"), float(eps), _form(form),
+                                                                 _ptr(y), _ptr(rstd), _stream(x2.device)))
     return y.reshape(x.shape), rstd
 
 
 def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor], weight: torch.Tensor, eps: float,
-                need_param_grads: bool = True):
+                need_param_grads: bool = True, form: str = "cast_then_weight"):
     """Returns (dx, dweight).  rstd None: recomputed from x."""
     lib = _L()
     x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
@@ -228,9 +239,10 @@ def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor],
     dw = torch.empty(N, dtype=weight.dtype, device=x2.device) if need_param_grads else None
     with torch.cuda.device(x2.device):
         ws = _workspace("rmsnorm", M, N, x2.dtype, x2.device)
-        _lib.check(lib, "rmsnorm_bwd", lib.rmsnorm_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(rstd),
-                                                       _ptr(weight), _dt(weight, "weight"), float(eps), _ptr(dx),
-                                                       _ptr(dw), ws.data_ptr(), ws.numel(), _stream(x2.device)))
+        _lib.check(lib, "rmsnorm_bwd_form", lib.rmsnorm_bwd_form(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(rstd),
+                                                                 _ptr(weight), _dt(weight, "weight"), float(eps),
+                                                                 _form(form), _ptr(dx), _ptr(dw), ws.data_ptr(),
+                                                                 ws.numel(), _stream(x2.device)))
     return dx.reshape(x.shape), dw
 
 

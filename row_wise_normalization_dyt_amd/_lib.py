@@ -34,6 +34,8 @@ SIGNATURES = {
     "rmsnorm_fwd": (_ci, [_i64, _i64, _vp, _ci, _vp, _ci, _cf, _vp, _fp, _vp]),
     "rmsnorm_bwd": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _vp, _ci, _cf, _vp, _vp, _vp, _sz, _vp]),
     "rmsnorm_bwd_workspace_size": (_ci, [_i64, _i64, _ci, ctypes.POINTER(_sz)]),
+    "rmsnorm_fwd_form": (_ci, [_i64, _i64, _vp, _ci, _vp, _ci, _cf, _ci, _vp, _fp, _vp]),
+    "rmsnorm_bwd_form": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _vp, _ci, _cf, _ci, _vp, _vp, _vp, _sz, _vp]),
     "rwn_last_error": (ctypes.c_char_p, []),
     "rwn_version": (ctypes.c_char_p, []),
     "rwn_trace_begin": (_ci, [_ci]),

@@ -317,12 +317,21 @@ RWN_API rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype 
 
 // ================================================================================== RMSNorm
 
-RWN_API rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
-                               const void* weight, rwn_dtype weight_dtype, float eps, void* y,
-                               float* rstd, void* stream) {
-    const char* fn = "rmsnorm_fwd";
+namespace {
+
+rwn_status check_variant(const char* fn, int variant) {
+    if (variant != RWN_RMS_CAST_THEN_WEIGHT && variant != RWN_RMS_WEIGHT_THEN_CAST &&
+        variant != RWN_RMS_ONE_PLUS_WEIGHT)
+        return fail(RWN_ERR_INVALID_ARG, "%s: unknown RMSNorm form %d", fn, variant);
+    return RWN_OK;
+}
+
+rwn_status rms_fwd_impl(const char* fn, int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                        const void* weight, rwn_dtype weight_dtype, float eps, int variant, void* y,
+                        float* rstd, void* stream) {
     rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, weight_dtype);
     if (st != RWN_OK) return st;
+    if ((st = check_variant(fn, variant)) != RWN_OK) return st;
     if ((st = check_eps(fn, eps)) != RWN_OK) return st;
     if (!weight) return fail(RWN_ERR_INVALID_ARG, "%s: weight is required", fn);
     if (M == 0) return ok();
@@ -335,19 +344,19 @@ RWN_API rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_
     if ((st = plan_for(fn, LAYER_RMS, false, M, N, x_dtype, weight_dtype, mis, &p)) != RWN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = traced(RWN_K_RMS_FWD, s, [&] {
-        return launch_rms_fwd(p, x_dtype, weight_dtype, x, weight, eps, y, rstd, s);
+        return launch_rms_fwd(p, x_dtype, weight_dtype, variant, x, weight, eps, y, rstd, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 
-RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
-                               rwn_dtype x_dtype, const float* rstd, const void* weight,
-                               rwn_dtype weight_dtype, float eps, void* dx, void* dweight,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "rmsnorm_bwd";
+rwn_status rms_bwd_impl(const char* fn, int64_t M, int64_t N, const void* x, const void* dy,
+                        rwn_dtype x_dtype, const float* rstd, const void* weight,
+                        rwn_dtype weight_dtype, float eps, int variant, void* dx, void* dweight,
+                        void* workspace, size_t workspace_bytes, void* stream) {
     rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, weight_dtype);
     if (st != RWN_OK) return st;
+    if ((st = check_variant(fn, variant)) != RWN_OK) return st;
     if ((st = check_eps(fn, eps)) != RWN_OK) return st;
     if (!weight) return fail(RWN_ERR_INVALID_ARG, "%s: weight is required", fn);
     hipStream_t s = (hipStream_t)stream;
@@ -362,10 +371,43 @@ RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* 
     if ((st = check_workspace(fn, p, LAYER_RMS, workspace, workspace_bytes)) != RWN_OK) return st;
     float* ws = (float*)workspace;
     hipError_t e = traced(RWN_K_RMS_BWD, s, [&] {
-        return launch_rms_bwd(p, x_dtype, weight_dtype, x, dy, rstd, weight, eps, dx, ws, s);
+        return launch_rms_bwd(p, x_dtype, weight_dtype, variant, x, dy, rstd, weight, eps, dx, ws, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return finish_bwd(fn, weight_dtype, ws, p.partial_rows(), ng, p.ws_rs, p.ws_cs, N, dweight, nullptr, nullptr, s);
+}
+
+}  // namespace
+
+RWN_API rwn_status rmsnorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                               const void* weight, rwn_dtype weight_dtype, float eps, void* y,
+                               float* rstd, void* stream) {
+    return rms_fwd_impl("rmsnorm_fwd", M, N, x, x_dtype, weight, weight_dtype, eps,
+                        RWN_RMS_CAST_THEN_WEIGHT, y, rstd, stream);
+}
+
+RWN_API rwn_status rmsnorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
+                               rwn_dtype x_dtype, const float* rstd, const void* weight,
+                               rwn_dtype weight_dtype, float eps, void* dx, void* dweight,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return rms_bwd_impl("rmsnorm_bwd", M, N, x, dy, x_dtype, rstd, weight, weight_dtype, eps,
+                        RWN_RMS_CAST_THEN_WEIGHT, dx, dweight, workspace, workspace_bytes, stream);
+}
+
+RWN_API rwn_status rmsnorm_fwd_form(int64_t M, int64_t N, const void* x, rwn_dtype x_dtype,
+                                    const void* weight, rwn_dtype weight_dtype, float eps,
+                                    rwn_rms_form form, void* y, float* rstd, void* stream) {
+    return rms_fwd_impl("rmsnorm_fwd_form", M, N, x, x_dtype, weight, weight_dtype, eps, (int)form,
+                        y, rstd, stream);
+}
+
+RWN_API rwn_status rmsnorm_bwd_form(int64_t M, int64_t N, const void* x, const void* dy,
+                                    rwn_dtype x_dtype, const float* rstd, const void* weight,
+                                    rwn_dtype weight_dtype, float eps, rwn_rms_form form, void* dx,
+                                    void* dweight, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    return rms_bwd_impl("rmsnorm_bwd_form", M, N, x, dy, x_dtype, rstd, weight, weight_dtype, eps,
+                        (int)form, dx, dweight, workspace, workspace_bytes, stream);
 }
 
 RWN_API rwn_status rmsnorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {

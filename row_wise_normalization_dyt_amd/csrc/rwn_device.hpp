@@ -59,6 +59,7 @@ struct Geom {
                       // column block w % ncb and strides over tiles by grid / ncb
     int xcd_remap;    // 1: renumber workgroups so consecutive numbers share an XCD (grid % 8 == 0)
     float inv_n;      // 1 / N
+    float w_offset;   // RMSNorm: added to the weight in float32 (1 for the (1 + weight) form)
 };
 
 // ------------------------------------------------------------------------- conversions

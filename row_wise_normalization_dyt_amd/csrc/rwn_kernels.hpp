@@ -605,7 +605,9 @@ __device__ __forceinline__ void rms_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
     for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+// VAR 0: the Llama form (normalized value rounded to x's dtype, then the weight multiply);
+// VAR 1: weight (plus g.w_offset) times the float32 normalized value, rounded once.
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps,
                T* __restrict__ y, float* __restrict__ rstd_out, Geom g) {
@@ -616,6 +618,10 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
     load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    if constexpr (VAR != 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[e] += g.w_offset;   // (1 + weight) in float32
+    }
     struct In {
         RowRegs<T, MODE, CPT> xr[RT];
         int64_t row[RT];
@@ -641,11 +647,14 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 float o[V];
-                // One rounding of the normalized value to x's dtype, then the weight multiply
-                // in float32; the store rounds the product to x's dtype.
+                // VAR 0: one rounding of the normalized value to x's dtype, then the weight
+                // multiply in float32.  VAR 1: the float32 product of the weight and the
+                // unrounded normalized value.  The store rounds the product to x's dtype.
 #pragma unroll
-                for (int v = 0; v < V; ++v)
-                    o[v] = w[k * V + v] * round_through<T>(xr[u].get(k, v) * rs[u]);
+                for (int v = 0; v < V; ++v) {
+                    const float h = xr[u].get(k, v) * rs[u];
+                    o[v] = w[k * V + v] * (VAR == 0 ? round_through<T>(h) : h);
+                }
                 store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o, ok[u]);
             }
             if (ok[u] && c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
@@ -654,7 +663,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                const PT* __restrict__ weight, float eps, T* __restrict__ dx,
@@ -667,6 +676,10 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
     load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    if constexpr (VAR != 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[e] += g.w_offset;   // (1 + weight) in float32
+    }
     float acc_w[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_w[e] = 0.f;
@@ -716,8 +729,10 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
             for (int k = 0; k < CPT; ++k)
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    // grad of the normalized value: the float32 product rounded to x's dtype.
-                    const float gg = round_through<T>(gr[u].get(k, v) * w[k * V + v]);
+                    // grad of the normalized value: the float32 product, rounded to x's dtype
+                    // in the Llama form (where the normalized value itself was rounded).
+                    const float p = gr[u].get(k, v) * w[k * V + v];
+                    const float gg = VAR == 0 ? round_through<T>(p) : p;
                     a = __builtin_fmaf(gg, xr[u].get(k, v) * rs[u], a);
                 }
             s[u] = a;
@@ -734,9 +749,11 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     const int e = k * V + v;
                     const float gv = gr[u].get(k, v);
                     const float h = xr[u].get(k, v) * rs[u];
-                    const float gg = round_through<T>(gv * w[e]);
-                    // weight-gradient term: dy * n rounded to the weight's dtype before the sum.
-                    const float term = round_through<PT>(gv * round_through<T>(h));
+                    const float gg = VAR == 0 ? round_through<T>(gv * w[e]) : gv * w[e];
+                    // weight-gradient term.  Llama form: dy * n, n = h rounded to x's dtype, the
+                    // product rounded to the weight's dtype before the sum.  Float32 forms:
+                    // dy * h, summed in float32 and rounded once at the end.
+                    const float term = VAR == 0 ? round_through<PT>(gv * round_through<T>(h)) : gv * h;
                     acc_w[e] += term;
                     o[v] = rs[u] * (gg - h * cc);
                 }

@@ -86,6 +86,7 @@ inline Geom make_geom(const Plan& p) {
     g.rpp = p.rpp;
     g.base_shift = p.base_shift;
     g.inv_n = 1.0f / (float)p.N;
+    g.w_offset = 0.0f;
     return g;
 }
 
@@ -177,9 +178,13 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
 hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                          const float* mean, const float* rstd, const void* gamma, float eps,
                          void* dx, float* ws, hipStream_t s);
-hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* w,
+// RMSNorm forms: the Llama form rounds the normalized value to x's dtype before the weight
+// multiply; the two others multiply in float32 and round once, by weight or by (1 + weight).
+enum RmsVariant { RMS_CAST_THEN_WEIGHT = 0, RMS_WEIGHT_THEN_CAST = 1, RMS_ONE_PLUS_WEIGHT = 2 };
+
+hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                           float eps, void* y, float* rstd, hipStream_t s);
-hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
                           const float* rstd, const void* w, float eps, void* dx, float* ws,
                           hipStream_t s);
 // Stage 2: P partial rows of ng columns (element (p, c) at ws[p * rs + c * cs]) ->

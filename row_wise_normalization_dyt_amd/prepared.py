@@ -9,12 +9,12 @@ from typing import Dict, Optional
 
 import torch
 
-from . import _lib, _like, _DT, workspace_size
+from . import _lib, _like, _DT, _form, workspace_size
 
 
 class PreparedStep:
     def __init__(self, layer: str, inputs: Dict[str, torch.Tensor], eps: float = 0.0,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None, form: str = "cast_then_weight"):
         self.layer = layer
         self.lib = lib = _lib.load()
         x, dy = inputs["x"], inputs["dy"]
@@ -57,9 +57,12 @@ class PreparedStep:
             wdt = _DT[w.dtype]
             self.rstd = torch.empty(M, dtype=torch.float32, device=dev)
             self.grads = {"dweight": torch.empty(N, dtype=w.dtype, device=dev)}
-            self._f, self._fa = lib.rmsnorm_fwd, (M, N, p(x), xdt, p(w), wdt, float(eps), p(self.y), p(self.rstd), s)
-            self._b, self._ba = lib.rmsnorm_bwd, (M, N, p(x), p(dy), xdt, p(self.rstd), p(w), wdt, float(eps),
-                                                  p(self.dx), p(self.grads["dweight"]), p(self.ws), self.ws.numel(), s)
+            f = _form(form)
+            self._f, self._fa = lib.rmsnorm_fwd_form, (M, N, p(x), xdt, p(w), wdt, float(eps), f, p(self.y),
+                                                       p(self.rstd), s)
+            self._b, self._ba = lib.rmsnorm_bwd_form, (M, N, p(x), p(dy), xdt, p(self.rstd), p(w), wdt, float(eps), f,
+                                                       p(self.dx), p(self.grads["dweight"]), p(self.ws),
+                                                       self.ws.numel(), s)
         else:
             raise ValueError(layer)
 

@@ -19,7 +19,8 @@ import workloads
 DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
-def gpu_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, use_stats: bool = True) -> Dict[str, torch.Tensor]:
+def gpu_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, use_stats: bool = True,
+            form: str = "cast_then_weight") -> Dict[str, torch.Tensor]:
     """Forward then backward on the tensors' device (dy is the upstream gradient of y)."""
     x, dy = inp["x"], inp["dy"]
     if layer == "dyt":
@@ -35,8 +36,8 @@ def gpu_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, use_stats: boo
         if use_stats:
             out.update(mean=mean, rstd=rstd)
         return out
-    y, rstd = rwn.rmsnorm_fwd(x, inp["weight"], eps)
-    dx, dw = rwn.rmsnorm_bwd(x, dy, rstd if use_stats else None, inp["weight"], eps)
+    y, rstd = rwn.rmsnorm_fwd(x, inp["weight"], eps, form=form)
+    dx, dw = rwn.rmsnorm_bwd(x, dy, rstd if use_stats else None, inp["weight"], eps, form=form)
     out = {"y": y, "dx": dx, "dweight": dw}
     if use_stats:
         out["rstd"] = rstd
@@ -44,7 +45,7 @@ def gpu_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, use_stats: boo
 
 
 def oracle_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, rows: Optional[Sequence[int]] = None,
-               grads: bool = True) -> Dict[str, np.ndarray]:
+               grads: bool = True, form: str = "cast_then_weight") -> Dict[str, np.ndarray]:
     """Oracle on host copies.  rows: compute y/dx (and stats) only for these rows; the
     parameter gradients always use every row."""
     h = {k: v.detach().cpu() for k, v in inp.items()}
@@ -69,11 +70,11 @@ def oracle_run(layer: str, inp: Dict[str, torch.Tensor], eps: float, rows: Optio
             out.update({k: v for k, v in (b if rows is None else oracle.layernorm_bwd(x, dy, g, e, want_dx=False)).items()
                         if k.startswith(("dgamma", "dbeta"))})
     else:
-        out.update(oracle.rmsnorm_fwd(xs, h["weight"], e))
-        b = oracle.rmsnorm_bwd(xs, dys, h["weight"], e)
+        out.update(oracle.rmsnorm_fwd(xs, h["weight"], e, form=form))
+        b = oracle.rmsnorm_bwd(xs, dys, h["weight"], e, form=form)
         out.update(dx=b["dx"], dx_scale=b["dx_scale"])
         if grads:
-            out.update({k: v for k, v in (b if rows is None else oracle.rmsnorm_bwd(x, dy, h["weight"], e, want_dx=False)).items()
+            out.update({k: v for k, v in (b if rows is None else oracle.rmsnorm_bwd(x, dy, h["weight"], e, want_dx=False, form=form)).items()
                         if k.startswith("dweight")})
     return out
 
@@ -108,9 +109,9 @@ def check_workload(wl: workloads.Workload, device="cuda", rows: Optional[Sequenc
     if inputs is None:
         inputs = workloads.make_inputs(wl, device if on_gpu_inputs else "cpu")
     dev_in = {k: v.to(device) for k, v in inputs.items()}
-    g = gpu_run(wl.layer, dev_in, wl.eps, use_stats)
+    g = gpu_run(wl.layer, dev_in, wl.eps, use_stats, form=wl.form)
     torch.cuda.synchronize()
-    o = oracle_run(wl.layer, inputs, wl.eps, rows=rows)
+    o = oracle_run(wl.layer, inputs, wl.eps, rows=rows, form=wl.form)
     return compare(wl.layer, g, o, DT[wl.xdt], DT[wl.pdt], rows=rows)
 
 

@@ -61,6 +61,9 @@ def test_dtype_errors(lib):
     assert lib.dyt_fwd(4, 8, P, 2, P, P, P, 1, P, None) == 2               # f16 x, bf16 params
     assert "float16 x with bfloat16 parameters" in _err(lib)
     assert lib.dyt_fwd(4, 8, P, 3, P, P, P, 0, P, None) == 1               # no dtype code 3
+    assert lib.rmsnorm_fwd_form(4, 8, P, 1, P, 1, 1e-6, 3, P, None, None) == 1   # no form 3
+    assert "form" in _err(lib)
+    assert lib.rmsnorm_bwd_form(4, 8, P, P, 1, None, P, 1, 1e-6, -1, P, P, P, 1 << 20, None) == 1
 
 
 def test_null_and_eps_errors(lib):

@@ -42,6 +42,13 @@ MUTANTS = [
      "int64_t i1 = ((b + 1) * ORA_ROW_BLOCK < M ? (b + 1) * ORA_ROW_BLOCK : M) - 1;"),
     ("bf16_ties_away", "double r = ldexp(nearbyint(ldexp(v, -q)), q);", "double r = ldexp(round(ldexp(v, -q)), q);"),
     ("bf16_seven_bits", "int q = e - 8;", "int q = e - 7;"),
+    ("rms_form_drops_one", "return form == 2 ? round_arith(xdt, 1.0 + wj) : wj;", "return wj;"),
+    ("rms_form_rounds_g", "double g = load_elem(dy, xdt, i * N + j) * rms_form_scale(form, xdt, load_elem(w, wdt, j));\n                double h = load_elem(x, xdt, i * N + j) * r;\n                if (dx)",
+     "double g = round_to(xdt, load_elem(dy, xdt, i * N + j) * rms_form_scale(form, xdt, load_elem(w, wdt, j)));\n                double h = load_elem(x, xdt, i * N + j) * r;\n                if (dx)"),
+    ("rms_form_rounds_h", "double v = rms_form_scale(form, xdt, load_elem(w, wdt, j)) * (load_elem(x, xdt, i * N + j) * r);",
+     "double v = rms_form_scale(form, xdt, load_elem(w, wdt, j)) * round_to(xdt, load_elem(x, xdt, i * N + j) * r);"),
+    ("rms_form_dw_drops_rstd", "terms[j] = load_elem(c->dy, c->xdt, i * c->N + j) * (load_elem(c->x, c->xdt, i * c->N + j) * r);",
+     "terms[j] = load_elem(c->dy, c->xdt, i * c->N + j) * load_elem(c->x, c->xdt, i * c->N + j);"),
     ("f16_nine_fraction_bits", "int q = e - 11;", "int q = e - 10;"),
     ("f16_subnormal_spacing", "if (q < -24) q = -24;", "if (q < -25) q = -25;"),
     ("f16_no_overflow", "if (fabs(r) > 65504.0) r = copysign(INFINITY, v);", ""),

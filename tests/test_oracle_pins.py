@@ -457,6 +457,84 @@ def test_rmsnorm_f16_matches_eager_expression():
     assert np.all(np.abs(ora_dw - eager_dw) <= 2 * ulpw)
 
 
+# The two float32 RMSNorm forms (DeepSpeed PR #8645, "Which modules are replaced" and "Not
+# covered"): weight before the cast, and (1 + weight).
+
+@pytest.mark.parametrize("form", ["weight_then_cast", "one_plus_weight"])
+def test_rmsnorm_float32_forms_match_torch_autograd_float64(form):
+    M, N, eps = 9, 40, 1e-6
+    x = _randn((M, N), 101).requires_grad_(True)
+    w = _randn(N, 102, scale=0.3, shift=0.2).requires_grad_(True)
+    dy = _randn((M, N), 103)
+    s = w if form == "weight_then_cast" else 1.0 + w
+    y = s * (x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + eps))
+    y.backward(dy)
+    fw = oracle.rmsnorm_fwd(x.detach(), w.detach(), eps, form=form)
+    bw = oracle.rmsnorm_bwd(x.detach(), dy, w.detach(), eps, form=form)
+    np.testing.assert_allclose(fw["y"], y.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(bw["dx"], x.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(bw["dweight"], w.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("form", ["weight_then_cast", "one_plus_weight"])
+def test_rmsnorm_float32_forms_exact_small_case(form):
+    """Exact rational arithmetic on x = [1, 7], eps = 0 (rstd = 1/5): no rounding of the
+    normalized value or of dy * s before use, and dweight = sum over rows of dy * h."""
+    xs = [Fraction(1), Fraction(7)]
+    ws = [Fraction(3), Fraction(193, 64)]
+    dys = [Fraction(3), Fraction(3)]
+    r = Fraction(1, 5)
+    sc = ws if form == "weight_then_cast" else [1 + w for w in ws]
+    h = [xv * r for xv in xs]
+    g = [d * sv for d, sv in zip(dys, sc)]
+    c = sum(gi * hi for gi, hi in zip(g, h)) / 2
+    dx = [r * (gi - hi * c) for gi, hi in zip(g, h)]
+    M = 4
+    to_bf16 = lambda vals, m: torch.tensor([[float(v) for v in vals]] * m, dtype=torch.float32).to(torch.bfloat16)
+    x = to_bf16(xs, M); dy = to_bf16(dys, M)
+    w = torch.tensor([float(v) for v in ws], dtype=torch.float32).to(torch.bfloat16)
+    assert _rne(dys[1] * sc[1]) != dys[1] * sc[1]          # rounding g would change it
+    fw = oracle.rmsnorm_fwd(x, w, 0.0, form=form)
+    bw = oracle.rmsnorm_bwd(x, dy, w, 0.0, form=form)
+    for j in range(2):
+        assert math.isclose(fw["y"][0, j], float(sc[j] * h[j]), rel_tol=1e-14)
+        assert math.isclose(bw["dx"][0, j], float(dx[j]), rel_tol=1e-13)
+        assert math.isclose(bw["dweight"][j], float(M * dys[j] * h[j]), rel_tol=1e-14)
+
+
+@pytest.mark.parametrize("form", ["weight_then_cast", "one_plus_weight"])
+def test_rmsnorm_float32_forms_match_eager_bf16(form):
+    """The forms' eager expressions in bfloat16 (float32 normalization, one float32 product,
+    one cast) against the oracle: y within one bf16 ulp and almost always equal."""
+    M, N = 64, 96
+    xb = _randn((M, N), 111, torch.float32).to(torch.bfloat16)
+    wb = _randn(N, 112, torch.float32, scale=0.1, shift=0.5).to(torch.bfloat16)
+    dyb = _randn((M, N), 113, torch.float32).to(torch.bfloat16)
+    eps = 1e-6
+    x = xb.clone().requires_grad_(True)
+    w = wb.clone().requires_grad_(True)
+    xf = x.float()
+    hf = xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps)
+    y = (w * hf).to(x.dtype) if form == "weight_then_cast" else (hf * (1.0 + w.float())).type_as(x)
+    y.backward(dyb)
+    fw = oracle.rmsnorm_fwd(xb, wb, float(np.float32(eps)), form=form)
+    ora_y = oracle.round_bf16(fw["y"])
+    eager_y = y.detach().double().numpy()
+    assert (ora_y == eager_y).mean() >= 0.99
+    ulp = np.exp2(np.floor(np.log2(np.abs(eager_y) + 1e-30)) - 7)
+    assert np.all(np.abs(ora_y - eager_y) <= ulp * 1.0001)
+    bw = oracle.rmsnorm_bwd(xb, dyb, wb, float(np.float32(eps)), form=form)
+    ora_dx = oracle.round_bf16(bw["dx"])
+    eager_dx = x.grad.double().numpy()
+    assert (ora_dx == eager_dx).mean() >= 0.9
+    ulpx = np.exp2(np.floor(np.log2(np.abs(eager_dx) + 1e-30)) - 7)
+    assert np.all(np.abs(ora_dx - eager_dx) <= 2 * ulpx + 1e-6 * bw["dx_scale"])
+    ora_dw = oracle.round_bf16(bw["dweight"])
+    eager_dw = w.grad.double().numpy()
+    ulpw = np.exp2(np.floor(np.log2(np.abs(eager_dw))) - 7)
+    assert np.all(np.abs(ora_dw - eager_dw) <= 2 * ulpw)
+
+
 def test_rmsnorm_alternative_rounding_is_rare_and_one_step():
     x = _randn((128, 64), 81, torch.float32).to(torch.bfloat16)
     w = _randn(64, 82, torch.float32, shift=1.0).to(torch.bfloat16)

@@ -60,6 +60,19 @@ def test_edge_widths(layer, xdt, pdt):
     tol.assert_reports(reps)
 
 
+@pytest.mark.parametrize("xdt,pdt", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16")])
+@pytest.mark.parametrize("form", ["weight_then_cast", "one_plus_weight"])
+def test_rmsnorm_float32_forms(form, xdt, pdt):
+    """The weight-before-cast and (1 + weight) RMSNorm forms over aligned, shifted and narrow
+    shapes, with the weight's mean at 0 so that (1 + weight) differs from weight."""
+    reps = []
+    for (M, N) in [(4099, 24), (777, 128), (263, 1024), (67, 4096), (257, 1025), (65, 17), (7, 2049)]:
+        wl = workloads.small("rmsnorm", M, N, xdt, pdt, seed=M + N, form=form, gamma_mean=0.0, gamma_std=0.5)
+        _banner(wl)
+        reps += gc.check_workload(wl, DEV)
+    tol.assert_reports(reps)
+
+
 @pytest.mark.parametrize("layer", LAYERS)
 def test_edge_row_counts(layer):
     reps = []

@@ -53,7 +53,8 @@ class Workload:
     gamma_std: float = 0.1
     beta_mean: float = 0.0
     beta_std: float = 0.1
-    alpha: float = 0.5            # DyT only
+    alpha: float = 0.5
+    form: str = "cast_then_weight"  # RMSNorm form: cast_then_weight | weight_then_cast | one_plus_weight            # DyT only
     eps: float = 1e-5             # LayerNorm / RMSNorm only
 
     def with_shape(self, M: int, N: Optional[int] = None) -> "Workload":
@@ -119,6 +120,10 @@ def standard_workloads() -> Dict[str, Workload]:
                       ("wide_layernorm_bf16_65536x4096", "f32")):
         name = base.replace("bf16", "f16")
         w[name] = dataclasses.replace(w[base], name=name, xdt="f16", pdt=pdt)
+    # The two float32 RMSNorm forms at configuration 4's first shape.
+    for form in ("weight_then_cast", "one_plus_weight"):
+        name = f"rmsnorm_{form}_bf16_16384x2048"
+        w[name] = dataclasses.replace(w["rmsnorm_bf16_16384x2048"], name=name, form=form)
     return w
 
 
