@@ -143,10 +143,13 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         int64_t best_waste = -1;
         const int order_dyt[3] = {1, 4, 2}, order_norm[3] = {2, 4, 1}, order_few_waves[3] = {4, 2, 1};
         const int* order = layer == LAYER_DYT ? order_dyt : order_norm;
-        // A SHIFTED RMSNorm forward runs fastest with the fewest waves per row (measured at
-        // N = 1025: one wave with four chunks per lane beats three waves with one), idle lanes
-        // notwithstanding: no cross-wave combine, and its one reduction has no masked terms.
-        const bool few_waves = layer == LAYER_RMS && !backward && p.mode == MODE_SHIFTED;
+        // SHIFTED RMSNorm forwards run fastest with the fewest waves per row, and so do SHIFTED
+        // LayerNorm forwards whose row fits one wave (measured at N = 1025 bf16: one wave with
+        // four chunks per lane against three waves with one, RMSNorm 62 vs 72 us, LayerNorm 80.6
+        // vs 91.1 us), idle lanes notwithstanding: no cross-wave combine, so no barrier between
+        // a row's loads and its stores.
+        const bool few_waves = !backward && p.mode == MODE_SHIFTED &&
+                               (layer == LAYER_RMS || (layer == LAYER_LN && chunks <= 4 * 64));
         if (few_waves) order = order_few_waves;
         for (int oi = 0; oi < 3; ++oi) {
             const int cpt = order[oi];
