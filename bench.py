@@ -82,7 +82,7 @@ def time_workload(wl, steps: int, warmup: int, trace: bool = True):
     sets = []
     for i in range(nsets):
         inp = base if i == 0 else {k: v.clone() for k, v in base.items()}
-        sets.append(PreparedStep(wl.layer, inp, wl.eps, form=wl.form))
+        sets.append(PreparedStep(wl.layer, inp, wl.eps, form=wl.form, param_grads=wl.param_grads))
     for i in range(warmup):
         sets[i % nsets].step()
     torch.cuda.synchronize()

@@ -35,7 +35,9 @@
  *            atomic-free reduction: per-workgroup float32 partial rows in the caller's workspace,
  *            then a fixed-order float64 pass over them.  Results are bitwise reproducible run
  *            to run for the same inputs, device and library build.  A NULL gradient pointer
- *            skips writing that gradient.
+ *            skips writing that gradient; when every gradient pointer of a call is NULL the
+ *            backward computes dx only (no column partials, no second pass) and the workspace
+ *            may be NULL.
  * Gradients  First-order only; eps is a constant.
  * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16 or
  *            float16 elements) spread over at most 1024 threads; when N is not a multiple of the chunk

@@ -138,9 +138,9 @@ def dyt_bwd(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch
     dg = torch.empty(N, dtype=gamma.dtype, device=x2.device) if need_param_grads else None
     db = torch.empty(N, dtype=gamma.dtype, device=x2.device) if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("dyt", M, N, x2.dtype, x2.device)
+        ws = _workspace("dyt", M, N, x2.dtype, x2.device) if need_param_grads else None
         _lib.check(lib, "dyt_bwd", lib.dyt_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(alpha), _ptr(gamma), pdt,
-                                               _ptr(dx), _ptr(da), _ptr(dg), _ptr(db), ws.data_ptr(), ws.numel(),
+                                               _ptr(dx), _ptr(da), _ptr(dg), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
                                                _stream(x2.device)))
     return dx.reshape(x.shape), da, dg, db
 
@@ -186,10 +186,10 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
     dg = torch.empty(N, dtype=pdtype, device=x2.device) if need_param_grads else None
     db = torch.empty(N, dtype=pdtype, device=x2.device) if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("layernorm", M, N, x2.dtype, x2.device)
+        ws = _workspace("layernorm", M, N, x2.dtype, x2.device) if need_param_grads else None
         _lib.check(lib, "layernorm_bwd", lib.layernorm_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(mean),
                                                            _ptr(rstd), _ptr(gamma), _DT[pdtype], float(eps),
-                                                           _ptr(dx), _ptr(dg), _ptr(db), ws.data_ptr(), ws.numel(),
+                                                           _ptr(dx), _ptr(dg), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
                                                            _stream(x2.device)))
     return dx.reshape(x.shape), dg, db
 
@@ -238,11 +238,11 @@ def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor],
     dx = _like(x2)
     dw = torch.empty(N, dtype=weight.dtype, device=x2.device) if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("rmsnorm", M, N, x2.dtype, x2.device)
+        ws = _workspace("rmsnorm", M, N, x2.dtype, x2.device) if need_param_grads else None
         _lib.check(lib, "rmsnorm_bwd_form", lib.rmsnorm_bwd_form(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(rstd),
                                                                  _ptr(weight), _dt(weight, "weight"), float(eps),
-                                                                 _form(form), _ptr(dx), _ptr(dw), ws.data_ptr(),
-                                                                 ws.numel(), _stream(x2.device)))
+                                                                 _form(form), _ptr(dx), _ptr(dw), _ptr(ws),
+                                                                 0 if ws is None else ws.numel(), _stream(x2.device)))
     return dx.reshape(x.shape), dw
 
 

@@ -28,17 +28,19 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
                           const void* alpha, const void* gamma, void* dx, float* ws,
                           hipStream_t s) {
     const Geom g = make_geom(p);
-    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
-        using T = typename decltype(tt)::type;
-        using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
-            constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
-            if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
-            else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
-            else return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value, decltype(pf)::value>,
-                               dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
-                               (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, g);
+    return dispatch_pg(ws, [&](auto pg) {
+        return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+            using T = typename decltype(tt)::type;
+            using PT = typename decltype(pt)::type;
+            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+                constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
+                if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
+                else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+                else return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                                  decltype(rt)::value, decltype(pf)::value, decltype(pg)::value>,
+                                   dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
+                                   (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, g);
+            });
         });
     });
 }
@@ -53,7 +55,7 @@ int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt) {
             else {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
                 constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
-                const void* k = backward ? (const void*)dyt_bwd_kernel<T, PT, M_, C_, R_, P_>
+                const void* k = backward ? (const void*)dyt_bwd_kernel<T, PT, M_, C_, R_, P_, 1>
                                          : (const void*)dyt_fwd_kernel<T, PT, M_, C_, R_, P_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;

@@ -26,16 +26,18 @@ hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const v
                          const float* mean, const float* rstd, const void* gamma, float eps,
                          void* dx, float* ws, hipStream_t s) {
     const Geom g = make_geom(p);
-    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
-        using T = typename decltype(tt)::type;
-        using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
-            constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
-            if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
-            return launch(ln_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                              decltype(rt)::value, decltype(pf)::value>,
-                               dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
-                               (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
+    return dispatch_pg(ws, [&](auto pg) {
+        return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+            using T = typename decltype(tt)::type;
+            using PT = typename decltype(pt)::type;
+            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+                constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
+                if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
+                return launch(ln_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
+                                            decltype(rt)::value, decltype(pf)::value, decltype(pg)::value>,
+                              dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
+                              (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
+            });
         });
     });
 }
@@ -49,7 +51,7 @@ int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt) {
             {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
                 constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
-                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_>
+                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_, 1>
                                          : (const void*)ln_fwd_kernel<T, PT, M_, C_, R_, P_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;

@@ -242,8 +242,10 @@ RWN_API rwn_status dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, 
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
     if ((st = plan_for(fn, LAYER_DYT, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
-    if ((st = check_workspace(fn, p, LAYER_DYT, workspace, workspace_bytes)) != RWN_OK) return st;
-    float* ws = (float*)workspace;
+    // No parameter gradient wanted: dx only, no workspace, no stage 2.
+    const bool grads = dgamma || dbeta || dalpha;
+    if (grads && (st = check_workspace(fn, p, LAYER_DYT, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = grads ? (float*)workspace : nullptr;
     hipError_t e = traced(RWN_K_DYT_BWD, s, [&] {
         return launch_dyt_bwd(p, x_dtype, param_dtype, x, dy, alpha, gamma, dx, ws, s);
     });
@@ -302,8 +304,10 @@ RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
     if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
-    if ((st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
-    float* ws = (float*)workspace;
+    // No parameter gradient wanted: dx only, no workspace, no stage 2.
+    const bool grads = dgamma || dbeta;
+    if (grads && (st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = grads ? (float*)workspace : nullptr;
     hipError_t e = traced(RWN_K_LN_BWD, s, [&] {
         return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, s);
     });
@@ -368,8 +372,10 @@ rwn_status rms_bwd_impl(const char* fn, int64_t M, int64_t N, const void* x, con
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
     if ((st = plan_for(fn, LAYER_RMS, true, M, N, x_dtype, weight_dtype, mis, &p)) != RWN_OK) return st;
-    if ((st = check_workspace(fn, p, LAYER_RMS, workspace, workspace_bytes)) != RWN_OK) return st;
-    float* ws = (float*)workspace;
+    // No parameter gradient wanted: dx only, no workspace, no stage 2.
+    const bool grads = dweight;
+    if (grads && (st = check_workspace(fn, p, LAYER_RMS, workspace, workspace_bytes)) != RWN_OK) return st;
+    float* ws = grads ? (float*)workspace : nullptr;
     hipError_t e = traced(RWN_K_RMS_BWD, s, [&] {
         return launch_rms_bwd(p, x_dtype, weight_dtype, variant, x, dy, rstd, weight, eps, dx, ws, s);
     });

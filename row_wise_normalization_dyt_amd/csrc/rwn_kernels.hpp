@@ -293,7 +293,9 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
     tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+// PG 0: no parameter gradient is wanted; the kernel computes dx only (no column partials,
+// nothing written to the workspace, which may be NULL).
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws,
@@ -351,16 +353,20 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
                         const float d = gv * ga[e];
                         if constexpr (decltype(finite)::value) {
                             const float ds = d * ts.s;   // dy * gamma * sech^2
-                            acc_g[e] = __builtin_fmaf(gv, ts.t, acc_g[e]);
-                            acc_b[e] += gv;
-                            acc_a = __builtin_fmaf(xv, ds, acc_a);
+                            if constexpr (PG) {
+                                acc_g[e] = __builtin_fmaf(gv, ts.t, acc_g[e]);
+                                acc_b[e] += gv;
+                                acc_a = __builtin_fmaf(xv, ds, acc_a);
+                            }
                             o[v] = alpha * ds;
                         } else {
                             const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
-                            const bool live = in.ok[u] && c.cm.valid(k, v, g.N);
-                            acc_g[e] += live ? gv * ts.t : 0.f;
-                            acc_b[e] += live ? gv : 0.f;
-                            acc_a += live ? d * xv * ts.s : 0.f;
+                            if constexpr (PG) {
+                                const bool live = in.ok[u] && c.cm.valid(k, v, g.N);
+                                acc_g[e] += live ? gv * ts.t : 0.f;
+                                acc_b[e] += live ? gv : 0.f;
+                                acc_a += live ? d * xv * ts.s : 0.f;
+                            }
                             o[v] = d * as;
                         }
                     }
@@ -374,11 +380,13 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
     tile_loop<PF, In>(c, fetch, body);
     // Partial row c.wg; this workgroup's column block of dgamma | dbeta, and its own dalpha
     // column 2N + cblk (stage 2 adds the ncb dalpha columns together).
-    float* out = ws + c.wg * g.ws_rs;
-    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
-    write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
-    const float da = block_sum(acc_a, red);
-    if (threadIdx.x == 0) out[(2 * g.N + c.cblk) * g.ws_cs] = da;
+    if constexpr (PG) {
+        float* out = ws + c.wg * g.ws_rs;
+        write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+        write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
+        const float da = block_sum(acc_a, red);
+        if (threadIdx.x == 0) out[(2 * g.N + c.cblk) * g.ws_cs] = da;
+    }
 }
 
 // ============================================================================ LayerNorm
@@ -475,7 +483,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
     tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
               const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
@@ -567,8 +575,10 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     const int e = k * V + v;
                     const float gv = gr[u].get(k, v);
                     const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
-                    acc_g[e] = __builtin_fmaf(gv, xh, acc_g[e]);
-                    acc_b[e] += gv;
+                    if constexpr (PG) {
+                        acc_g[e] = __builtin_fmaf(gv, xh, acc_g[e]);
+                        acc_b[e] += gv;
+                    }
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
                 put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
@@ -576,9 +586,11 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         }
     };
     tile_loop<PF, In>(c, fetch, body);
-    float* out = ws + c.wg * g.ws_rs;
-    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
-    write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
+    if constexpr (PG) {
+        float* out = ws + c.wg * g.ws_rs;
+        write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+        write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
+    }
 }
 
 // ============================================================================== RMSNorm
@@ -663,7 +675,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR, int PG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                const PT* __restrict__ weight, float eps, T* __restrict__ dx,
@@ -753,8 +765,10 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     // weight-gradient term.  Llama form: dy * n, n = h rounded to x's dtype, the
                     // product rounded to the weight's dtype before the sum.  Float32 forms:
                     // dy * h, summed in float32 and rounded once at the end.
-                    const float term = VAR == 0 ? round_through<PT>(gv * round_through<T>(h)) : gv * h;
-                    acc_w[e] += term;
+                    if constexpr (PG) {
+                        const float term = VAR == 0 ? round_through<PT>(gv * round_through<T>(h)) : gv * h;
+                        acc_w[e] += term;
+                    }
                     o[v] = rs[u] * (gg - h * cc);
                 }
                 put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
@@ -762,8 +776,10 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
         }
     };
     tile_loop<PF, In>(c, fetch, body);
-    float* out = ws + c.wg * g.ws_rs;
-    write_partial<T, MODE, CPT>(out, g.ws_cs, acc_w, c.cm, c.slot, c.lane, g, part);
+    if constexpr (PG) {
+        float* out = ws + c.wg * g.ws_rs;
+        write_partial<T, MODE, CPT>(out, g.ws_cs, acc_w, c.cm, c.slot, c.lane, g, part);
+    }
 }
 
 // ============================================================================ stage 2

@@ -92,6 +92,13 @@ inline Geom make_geom(const Plan& p) {
 
 template <typename T> struct TypeTag { using type = T; };
 
+// Backward stage 1 with (PG = 1) or without (PG = 0) parameter-gradient partials: a NULL
+// workspace means no parameter gradient is wanted.
+template <typename F>
+hipError_t dispatch_pg(const float* ws, F&& f) {
+    return ws ? f(IC<1>{}) : f(IC<0>{});
+}
+
 // Calls f(TypeTag<T>, TypeTag<PT>) for the supported dtype pairs.
 template <typename F>
 hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {

@@ -14,7 +14,8 @@ from . import _lib, _like, _DT, _form, workspace_size
 
 class PreparedStep:
     def __init__(self, layer: str, inputs: Dict[str, torch.Tensor], eps: float = 0.0,
-                 stream: Optional[torch.cuda.Stream] = None, form: str = "cast_then_weight"):
+                 stream: Optional[torch.cuda.Stream] = None, form: str = "cast_then_weight",
+                 param_grads: bool = True):
         self.layer = layer
         self.lib = lib = _lib.load()
         x, dy = inputs["x"], inputs["dy"]
@@ -24,10 +25,13 @@ class PreparedStep:
         self.stream = (stream or torch.cuda.current_stream(dev)).cuda_stream
         xdt = _DT[x.dtype]
         self.y, self.dx = _like(x), _like(x)
-        ws_bytes = workspace_size(layer, M, N, x.dtype, dev)
-        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        # Without parameter gradients the backward computes dx only and takes no workspace.
+        ws_bytes = workspace_size(layer, M, N, x.dtype, dev) if param_grads else 0
+        self.ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if param_grads else None
         self.inputs = inputs
         p = lambda t: None if t is None else t.data_ptr()
+        wsn = self.ws.numel() if param_grads else 0
+        gp = lambda name: p(self.grads[name]) if param_grads else None   # NULL: gradient not wanted
         s = self.stream
         if layer == "dyt":
             a, g, b = inputs["alpha"], inputs["gamma"], inputs["beta"]
@@ -37,8 +41,8 @@ class PreparedStep:
                           "dbeta": torch.empty(N, dtype=g.dtype, device=dev)}
             self._f, self._fa = lib.dyt_fwd, (M, N, p(x), xdt, p(a), p(g), p(b), pdt, p(self.y), s)
             self._b, self._ba = lib.dyt_bwd, (M, N, p(x), p(dy), xdt, p(a), p(g), pdt, p(self.dx),
-                                              p(self.grads["dalpha"]), p(self.grads["dgamma"]),
-                                              p(self.grads["dbeta"]), p(self.ws), self.ws.numel(), s)
+                                              gp("dalpha"), gp("dgamma"),
+                                              gp("dbeta"), p(self.ws), wsn, s)
         elif layer == "layernorm":
             g, b = inputs.get("gamma"), inputs.get("beta")
             pdt = _DT[g.dtype] if g is not None else _lib.RWN_F32
@@ -50,8 +54,8 @@ class PreparedStep:
             self._f, self._fa = lib.layernorm_fwd, (M, N, p(x), xdt, p(g), p(b), pdt, float(eps), p(self.y),
                                                     p(self.mean), p(self.rstd), s)
             self._b, self._ba = lib.layernorm_bwd, (M, N, p(x), p(dy), xdt, p(self.mean), p(self.rstd), p(g), pdt,
-                                                    float(eps), p(self.dx), p(self.grads["dgamma"]),
-                                                    p(self.grads["dbeta"]), p(self.ws), self.ws.numel(), s)
+                                                    float(eps), p(self.dx), gp("dgamma"),
+                                                    gp("dbeta"), p(self.ws), wsn, s)
         elif layer == "rmsnorm":
             w = inputs["weight"]
             wdt = _DT[w.dtype]
@@ -61,10 +65,12 @@ class PreparedStep:
             self._f, self._fa = lib.rmsnorm_fwd_form, (M, N, p(x), xdt, p(w), wdt, float(eps), f, p(self.y),
                                                        p(self.rstd), s)
             self._b, self._ba = lib.rmsnorm_bwd_form, (M, N, p(x), p(dy), xdt, p(self.rstd), p(w), wdt, float(eps), f,
-                                                       p(self.dx), p(self.grads["dweight"]), p(self.ws),
-                                                       self.ws.numel(), s)
+                                                       p(self.dx), gp("dweight"), p(self.ws),
+                                                       wsn, s)
         else:
             raise ValueError(layer)
+        if not param_grads:
+            self.grads = {}
 
     def fwd(self) -> None:
         rc = self._f(*self._fa)

@@ -240,6 +240,36 @@ def test_dyt_alpha_edges_full_rows(alpha, N):
 FULL = [n for n in workloads.WORKLOADS]
 
 
+@pytest.mark.parametrize("layer", LAYERS)
+def test_dx_only_backward_matches_full_backward(layer):
+    """With every gradient pointer NULL (and no workspace) the backward computes dx alone; that
+    dx is bitwise the full backward's, at narrow, wide, shifted and scalar shapes and at the
+    headline size."""
+    shapes = [(4099, 24, "f32", "f32"), (1031, 128, "bf16", "f32"), (263, 1024, "bf16", "bf16"),
+              (257, 1025, "bf16", "f32"), (65, 17, "f16", "f16"), (67, 4096, "f32", "f32")]
+    if layer == "layernorm":
+        shapes.append((401408, 24, "f32", "f32"))
+    for (M, N, xdt, pdt) in shapes:
+        wl = workloads.small(layer, M, N, xdt, pdt, seed=M + N)
+        _banner(wl, "dx only")
+        inp = {k: v.to(DEV) for k, v in workloads.make_inputs(wl, DEV).items()}
+        x, dy = inp["x"], inp["dy"]
+        if layer == "dyt":
+            full = rwn.dyt_bwd(x, dy, inp["alpha"], inp["gamma"])
+            only = rwn.dyt_bwd(x, dy, inp["alpha"], inp["gamma"], need_param_grads=False)
+        elif layer == "layernorm":
+            _, mean, rstd = rwn.layernorm_fwd(x, inp["gamma"], inp["beta"], wl.eps)
+            full = rwn.layernorm_bwd(x, dy, mean, rstd, inp["gamma"], wl.eps)
+            only = rwn.layernorm_bwd(x, dy, mean, rstd, inp["gamma"], wl.eps, need_param_grads=False)
+        else:
+            _, rstd = rwn.rmsnorm_fwd(x, inp["weight"], wl.eps)
+            full = rwn.rmsnorm_bwd(x, dy, rstd, inp["weight"], wl.eps)
+            only = rwn.rmsnorm_bwd(x, dy, rstd, inp["weight"], wl.eps, need_param_grads=False)
+        torch.cuda.synchronize()
+        assert all(t is None for t in only[1:])
+        assert torch.equal(only[0].view(torch.uint8), full[0].view(torch.uint8)), wl.name
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(name):
     """Every workload at its real size, in the launch configuration the benchmark times:

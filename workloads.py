@@ -53,8 +53,9 @@ class Workload:
     gamma_std: float = 0.1
     beta_mean: float = 0.0
     beta_std: float = 0.1
-    alpha: float = 0.5
-    form: str = "cast_then_weight"  # RMSNorm form: cast_then_weight | weight_then_cast | one_plus_weight            # DyT only
+    alpha: float = 0.5            # DyT only
+    form: str = "cast_then_weight"  # RMSNorm form: cast_then_weight | weight_then_cast | one_plus_weight
+    param_grads: bool = True        # False: the backward is asked for dx only (frozen parameters)
     eps: float = 1e-5             # LayerNorm / RMSNorm only
 
     def with_shape(self, M: int, N: Optional[int] = None) -> "Workload":
@@ -83,7 +84,8 @@ class Workload:
         params = nparam_vec * self.N * sp + scalar
         fwd = 2 * self.elems * sx + stats + params
         # bwd reads x, dy, stats and the params it needs; writes dx and the param grads.
-        bwd_params = (self.N * sp + scalar) + params   # gamma (+alpha) read; grads written
+        # gamma (+alpha) read; grads written (none when only dx is asked for)
+        bwd_params = (self.N * sp + scalar) + (params if self.param_grads else 0)
         bwd = 3 * self.elems * sx + stats + bwd_params
         return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}
 
@@ -120,6 +122,10 @@ def standard_workloads() -> Dict[str, Workload]:
                       ("wide_layernorm_bf16_65536x4096", "f32")):
         name = base.replace("bf16", "f16")
         w[name] = dataclasses.replace(w[base], name=name, xdt="f16", pdt=pdt)
+    # Backwards asked for dx only (frozen parameters): no column partials and no second pass.
+    for base in ("layernorm_f32_401408x24", "dyt_bf16_1048573x128", "wide_rmsnorm_bf16_65536x4096"):
+        name = base + "_dx_only"
+        w[name] = dataclasses.replace(w[base], name=name, param_grads=False)
     # The two float32 RMSNorm forms at configuration 4's first shape.
     for form in ("weight_then_cast", "one_plus_weight"):
         name = f"rmsnorm_{form}_bf16_16384x2048"
