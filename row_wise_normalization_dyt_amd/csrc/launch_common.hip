@@ -105,13 +105,15 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     }
     const int v_elems = p.mode == MODE_SCALAR ? 1 : V;
     bool packed = false;   // DyT SHIFTED rows packed into workgroups without wave alignment
-    if (layer == LAYER_DYT && !backward && chunks > 64 && p.mode == MODE_SHIFTED && chunks <= 512 &&
+    if (layer == LAYER_DYT && chunks > 64 && p.mode == MODE_SHIFTED && chunks <= 512 &&
         packed_rows) {
         // DyT has no row reduction, so a row's lanes need not fill whole waves: a SHIFTED row
         // takes exactly `chunks` lanes, and as many rows as fit share a workgroup of <= 512
         // threads (N = 1025 bf16: 3 rows of 129 lanes, 387 of 448 lanes busy, against 129 of
-        // 192 with three whole waves per row; forward 85.8 -> 76.9 us).  The backward keeps
-        // whole-wave rows: its slot-by-slot combine of packed rows measured slower.
+        // 192 with three whole waves per row; forward 85.8 -> 76.9 us).  The backward packs its
+        // rows too, without pipelining (the pipelined form's registers leave too few waves
+        // resident for such workgroups): backward 120.8 -> 103.2 us, stage 2 7.7 -> 4.0 us (a
+        // third as many partial rows).
         p.tpr = (int)chunks;
         p.cpt = 1;
         packed = true;
@@ -209,7 +211,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         if (prefetch >= 0) p.pf = (prefetch == 2 && !(one && p.mode != MODE_SCALAR)) ? 1 : prefetch;
         else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
         else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
-        else p.pf = (p.mode == MODE_SHIFTED && one) ? 1 : 0;
+        else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
     }
     // Keep to the kernel shape's launch bound (tpr itself always fits: see the wave limits).
     const int maxb = max_block(p.rt, p.cpt, esz);
