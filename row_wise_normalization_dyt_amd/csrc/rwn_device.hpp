@@ -521,12 +521,14 @@ struct TanhSech2 { float t, s; };
 __device__ __forceinline__ TanhSech2 tanh_sech2(float z) {
     const float az = __builtin_fabsf(z);
     const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * az);   // 2 * log2(e)
-    const float q = __builtin_amdgcn_rcpf(1.0f + e);
-    const float tb = (1.0f - e) * q;
+    // q2 = 2 / (1 + e) from the halved denominator: scaling by 2 is exact, so t and s come out
+    // bitwise as from q = 1 / (1 + e), with one multiply less for s = e * q2 * q2 = 4e q^2.
+    const float q2 = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, e, 0.5f));
+    const float tb = __builtin_fmaf(-0.5f, e, 0.5f) * q2;
     const float ts = z * __builtin_fmaf(z * z, -0.33333333333333333f, 1.0f);
     TanhSech2 r;
     r.t = az < 0.03125f ? ts : __builtin_copysignf(tb, z);
-    r.s = 4.0f * e * q * q;
+    r.s = e * q2 * q2;
     return r;
 }
 
