@@ -24,13 +24,15 @@ static int64_t next_pow2(int64_t v) {
 
 // Tuning overrides, read once (each changes the launch plan, and with it the reduction order
 // and so the low bits of parameter gradients):
-//   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4)
+//   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4; default:
+//                           chosen per shape)
 //   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
 //   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
-//   RWN_XCD_REMAP           0: keep hardware workgroup numbering (default 1: XCD-contiguous)
+//   RWN_XCD_REMAP           0: keep hardware workgroup numbering, 1: XCD-contiguous numbering
+//                           (default: XCD-contiguous for rows of a wave or more only)
 //   RWN_WIDE_CPT            1, 2 or 4: chunks per thread of wide LayerNorm / RMSNorm rows
 //   RWN_PACKED_ROWS         0: SHIFTED DyT rows take whole waves (default 1: packed rows)
 //   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
@@ -72,12 +74,12 @@ static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pd
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
                int cus, bool occupancy, Plan* out) {
     static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
-    static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 1);
+    static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 0);
     static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
     static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
     static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
-    static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, 1);
+    static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, -1);
     static const int prefetch = env_int("RWN_PREFETCH", 0, 2, -1);
     static const int wide_cpt = env_int("RWN_WIDE_CPT", 1, 4, 0);
     static const int packed_rows = env_int("RWN_PACKED_ROWS", 0, 1, 1);
@@ -176,7 +178,11 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.tpr = 64 * best_w;
     }
     const bool narrow_aligned = p.mode == MODE_ALIGNED && p.cpt == 1 && p.tpr <= 64;
-    p.rt = narrow_aligned ? (backward ? bwd_rt : fwd_rt) : 1;
+    // Narrow DyT backwards of 32 lanes per row (N = 256 bf16) run fastest with two rows per
+    // thread and no pipelining (measured 311 -> 297 us at M = 1048573); other narrow shapes
+    // with one (two rows per thread measured 4.6% slower for LayerNorm N = 24 fp32).
+    const int bwd_rt_auto = (layer == LAYER_DYT && p.tpr >= 32) ? 2 : 1;
+    p.rt = narrow_aligned ? (backward ? (bwd_rt > 0 ? bwd_rt : bwd_rt_auto) : fwd_rt) : 1;
     if (p.rt == 3) p.rt = 2;
 
     // Row slots: narrow rows fill 256-thread workgroups; wide rows use wide_block threads.
@@ -282,7 +288,14 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         }
         p.grid = gt * p.ncb;
         p.kt = 0;
-        p.xcd_remap = (xcd_remap && p.grid % 8 == 0) ? 1 : 0;
+        // XCD-contiguous numbering pays where a row spans a wave or more (LayerNorm / RMSNorm
+        // 65536 x 4096..8192 bf16: 4-6% faster): neighbouring rows share cache lines at their
+        // ends, and both writers then sit behind one L2.  Narrow rows come in whole tiles that
+        // share no lines, and there the hardware's round-robin numbering streams faster
+        // (LayerNorm 401408 x 24 fp32 step 46.0 -> 44.1 us, DyT 1048573 x 128 bf16 forward
+        // 122 -> 103 us).
+        const bool remap = xcd_remap >= 0 ? xcd_remap == 1 : p.tpr >= 64;
+        p.xcd_remap = (remap && p.grid % 8 == 0) ? 1 : 0;
     }
     if (backward) {
         // Partials column-major when rows are short (stage 2 then reads each column
