@@ -186,13 +186,15 @@ int rwn_trace_end(float* ms, int* tags, int capacity);
 rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Launch plan the library chooses for an entry point (introspection for tests and tuning).
- * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 14 integers to out:
+ * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 15 integers to out:
  * {mode (0 aligned vectors, 1 shifted vectors, 2 scalar), chunks per thread, rows per thread,
  *  threads per row, row slots per workgroup, workgroup size, workgroups, row tiles,
  *  elements per chunk, row tiles per workgroup (0 when strided), strided (1: workgroup w
  *  visits tiles w, w + workgroups / column blocks, ...), column blocks per row, XCD remap
  *  (1: workgroup numbers renumbered so consecutive ones share an XCD), prefetch (1: the next
- *  tile's loads are issued before the current tile is processed)}.  param_dtype: the parameter
+ *  tile's loads are issued before the current tile is processed), flat (1: narrow aligned
+ *  LayerNorm rows through plain loads on clamped row indices instead of per-tile buffer
+ *  descriptors)}.  param_dtype: the parameter
  * dtype of a forward (-1: any; a backward is always planned for every parameter dtype, as its
  * workspace is).  misalign_bytes is the common address of x/y/dy/dx modulo 16.  cus: 0 plans
  * for the current device exactly as the entry points do (its CU count, and the workgroups of

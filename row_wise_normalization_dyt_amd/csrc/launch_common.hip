@@ -36,7 +36,9 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_WIDE_CPT            1, 2 or 4: chunks per thread of wide LayerNorm / RMSNorm rows
 //   RWN_PACKED_ROWS         0: SHIFTED DyT rows take whole waves (default 1: packed rows)
 //   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
-//                           they exist
+//                           they exist (and with it the general LayerNorm kernels)
+//   RWN_FLAT                0: narrow aligned LayerNorm rows take the general kernels (default 1:
+//                           the flat kernels)
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -83,6 +85,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int prefetch = env_int("RWN_PREFETCH", 0, 2, -1);
     static const int wide_cpt = env_int("RWN_WIDE_CPT", 1, 4, 0);
     static const int packed_rows = env_int("RWN_PACKED_ROWS", 0, 1, 1);
+    static const int flat_rows = env_int("RWN_FLAT", 0, 1, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -218,6 +221,14 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
         else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
         else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
+    }
+    // Narrow aligned LayerNorm rows, one chunk and one row per thread, take the flat kernels
+    // (plain loads on clamped row indices, no per-tile descriptors), which run fastest without
+    // pipelining.
+    if (flat_rows && prefetch < 0 && layer == LAYER_LN && p.mode == MODE_ALIGNED && p.cpt == 1 &&
+        p.rt == 1 && p.tpr <= 64 && p.ncb == 1) {
+        p.flat = 1;
+        p.pf = 0;
     }
     // Keep to the kernel shape's launch bound (tpr itself always fits: see the wave limits).
     const int maxb = max_block(p.rt, p.cpt, esz);

@@ -593,6 +593,136 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
     }
 }
 
+// ------------------------------------------------------------ LayerNorm, flat narrow rows
+// Narrow aligned rows (TPR <= 64 lanes per row, one 16-byte chunk per lane, one row per thread
+// per tile, no pipelining) through plain global loads and stores instead of per-tile buffer
+// descriptors.  A padded row loads the tensor's last row (a clamped index, always in bounds)
+// and a lane past the row's chunks loads the row's first chunk; both are zeroed after the
+// load, so every term they feed is 0, as with the descriptors' zero reads.  The group size and
+// whether the forward's statistics are given are template values, so a tile is one straight
+// line: its loads (x, dy and both statistics) issue together, and the row sums are fixed DPP
+// sequences.  The arithmetic, its order, the partial rows and their combine are those of the
+// general kernels.  (LayerNorm 401408 x 24 float32, measured: backward stage 1 23.7 -> 23.2 us,
+// dx only 21.4 -> 20.6 us.)
+template <typename T>
+__device__ __forceinline__ void load_flat(const T* __restrict__ p, int64_t off, bool keep,
+                                          RowRegs<T, MODE_ALIGNED, 1>& r) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + off));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r.w[0][w] = keep ? v[w] : 0u;
+}
+
+// Mean and rstd of one row from its lanes' chunks (lanes past the row hold zeros).
+template <typename T, int TPR>
+__device__ __forceinline__ void ln_stats_flat(const RowRegs<T, MODE_ALIGNED, 1>& xr, bool lane_in,
+                                              const Geom& g, float eps, float& mu, float& rs) {
+    constexpr int V = Elems<T, MODE_ALIGNED>::value;
+    float a = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) a += xr.get(0, v);
+    mu = group_sum(a, TPR) * g.inv_n;
+    a = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const float d = xr.get(0, v) - mu;
+        a += lane_in ? d * d : 0.f;
+    }
+    rs = __builtin_amdgcn_rsqf(group_sum(a, TPR) * g.inv_n + eps);
+}
+
+template <typename T, typename PT, int TPR>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256)))
+ln_fwd_flat_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta,
+                   float eps, T* __restrict__ y, float* __restrict__ mean_out,
+                   float* __restrict__ rstd_out, Geom g) {
+    constexpr int V = Elems<T, MODE_ALIGNED>::value;
+    RowCtx<T, MODE_ALIGNED, 1, 1> c(g);
+    float ga[V], be[V];
+    load_param_or<T, PT, MODE_ALIGNED, 1>(gamma, 1.f, g.N, c.cm, ga);
+    load_param_or<T, PT, MODE_ALIGNED, 1>(beta, 0.f, g.N, c.cm, be);
+    const bool lane_in = c.cm.any[0];
+    const int64_t col = lane_in ? c.cm.col0[0] : 0;
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+        const int64_t row = tile * c.rows_per_tile + c.slot;
+        const bool ok = row < g.M;
+        RowRegs<T, MODE_ALIGNED, 1> xr;
+        load_flat<T>(x, (ok ? row : g.M - 1) * g.N + col, lane_in, xr);
+        float mu, rs;
+        ln_stats_flat<T, TPR>(xr, lane_in, g, eps, mu, rs);
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = __builtin_fmaf((xr.get(0, v) - mu) * rs, ga[v], be[v]);
+        if (ok && lane_in)
+            __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(y + row * g.N + col));
+        if (ok && c.lane == 0) {
+            if (mean_out) mean_out[row] = mu;
+            if (rstd_out) rstd_out[row] = rs;
+        }
+    }
+}
+
+// ST: the forward's statistics are given (1) or recomputed from x (0).
+template <typename T, typename PT, int TPR, int PG, int ST>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256)))
+ln_bwd_flat_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
+                   const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
+                   T* __restrict__ dx, float* __restrict__ ws, Geom g) {
+    constexpr int V = Elems<T, MODE_ALIGNED>::value;
+    extern __shared__ float part[];
+    RowCtx<T, MODE_ALIGNED, 1, 1> c(g);
+    float ga[V];
+    load_param_or<T, PT, MODE_ALIGNED, 1>(gamma, 1.f, g.N, c.cm, ga);
+    const bool lane_in = c.cm.any[0];
+    const int64_t col = lane_in ? c.cm.col0[0] : 0;
+    float acc_g[V], acc_b[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc_g[v] = acc_b[v] = 0.f;
+    for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
+        const int64_t row = tile * c.rows_per_tile + c.slot;
+        const bool ok = row < g.M;
+        const int64_t lr = ok ? row : g.M - 1;
+        RowRegs<T, MODE_ALIGNED, 1> xr, gr;
+        load_flat<T>(x, lr * g.N + col, lane_in && ok, xr);
+        load_flat<T>(dy, lr * g.N + col, lane_in && ok, gr);
+        float mu, rs;
+        if constexpr (ST) {
+            mu = mean_in[lr];
+            rs = rstd_in[lr];
+        } else {
+            ln_stats_flat<T, TPR>(xr, lane_in, g, eps, mu, rs);
+        }
+        mu = ok ? mu : 0.f;
+        rs = ok ? rs : 0.f;
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const float xh = (xr.get(0, v) - mu) * rs;
+            const float gg = gr.get(0, v) * ga[v];
+            a += gg;
+            b = __builtin_fmaf(gg, xh, b);
+        }
+        const float c1 = group_sum(a, TPR) * g.inv_n, c2 = group_sum(b, TPR) * g.inv_n;
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const float gv = gr.get(0, v);
+            const float xh = (xr.get(0, v) - mu) * rs;
+            if constexpr (PG) {
+                acc_g[v] = __builtin_fmaf(gv, xh, acc_g[v]);
+                acc_b[v] += gv;
+            }
+            o[v] = rs * (gv * ga[v] - c1 - xh * c2);
+        }
+        if (ok && lane_in)
+            __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(dx + row * g.N + col));
+    }
+    if constexpr (PG) {
+        float* out = ws + c.wg * g.ws_rs;
+        write_partial<T, MODE_ALIGNED, 1>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+        write_partial<T, MODE_ALIGNED, 1>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
+    }
+}
+
 // ============================================================================== RMSNorm
 
 template <typename T, int MODE, int CPT, int RT>

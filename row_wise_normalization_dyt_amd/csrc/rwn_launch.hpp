@@ -37,6 +37,7 @@ struct Plan {
     int strided = 0;          // 1: grid-stride over tiles (grid * rpp a multiple of V)
     int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
     int xcd_remap = 0;        // renumber workgroups XCD-contiguously (needs grid % 8 == 0)
+    int flat = 0;             // LayerNorm narrow aligned rows through the flat kernels
     int pf = 0;               // software-pipelined tile loop: 0 off, 1 one tile ahead (cpt * rt <= 2),
                               // 2 two tiles ahead (cpt * rt == 1, vector modes)
     int base_shift = 0;       // SHIFTED: base misalignment in elements
@@ -185,6 +186,14 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
 hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                          const float* mean, const float* rstd, const void* gamma, float eps,
                          void* dx, float* ws, hipStream_t s);
+// The flat LayerNorm kernels of narrow aligned rows (plans with p.flat set).
+hipError_t launch_ln_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
+                              const void* beta, float eps, void* y, float* mean, float* rstd,
+                              hipStream_t s);
+hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                              const float* mean, const float* rstd, const void* gamma, float eps,
+                              void* dx, float* ws, hipStream_t s);
+int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt);
 // RMSNorm forms: the Llama form rounds the normalized value to x's dtype before the weight
 // multiply; the two others multiply in float32 and round once, by weight or by (1 + weight).
 enum RmsVariant { RMS_CAST_THEN_WEIGHT = 0, RMS_WEIGHT_THEN_CAST = 1, RMS_ONE_PLUS_WEIGHT = 2 };
