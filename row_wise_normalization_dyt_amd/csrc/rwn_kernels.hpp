@@ -612,6 +612,46 @@ __device__ __forceinline__ void load_flat(const T* __restrict__ p, int64_t off, 
     for (int w = 0; w < 4; ++w) r.w[0][w] = keep ? v[w] : 0u;
 }
 
+// Per-thread setup of the flat kernels, kept short: every workgroup runs it before its first
+// load.  The group size is a constant, there is one column block, the tiles keep the hardware's
+// workgroup numbering (narrow rows stream faster with it), and the parameters are loaded
+// branch-free.
+template <typename T, typename PT, int TPR>
+struct FlatCtx {
+    static constexpr int V = Elems<T, MODE_ALIGNED>::value;
+    int slot, lane;
+    bool lane_in;        // this lane holds a chunk of its row
+    int64_t col;         // column of the chunk (0 for lanes past the row)
+    int64_t rows_per_tile, t_begin, t_end, t_step, wg;
+    ColMap<T, MODE_ALIGNED, 1> cm;
+    __device__ __forceinline__ FlatCtx(const Geom& g) {
+        slot = threadIdx.x / TPR;
+        lane = threadIdx.x % TPR;
+        wg = blockIdx.x;
+        rows_per_tile = g.rpp;
+        if (g.strided) {
+            t_begin = wg;
+            t_end = g.ntiles;
+            t_step = gridDim.x;
+        } else {
+            t_begin = wg * g.kt;
+            t_end = t_begin + g.kt < g.ntiles ? t_begin + g.kt : g.ntiles;
+            t_step = 1;
+        }
+        cm.init(lane, TPR, g.N, 0, 0);
+        lane_in = cm.any[0];
+        col = lane_in ? cm.col0[0] : 0;
+    }
+    // V parameters of this lane's columns (`dflt` for a NULL vector), 0 past the row.
+    __device__ __forceinline__ void param(const PT* __restrict__ p, float dflt, float* o) const {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const float val = p ? to_f32(p[col + v]) : dflt;
+            o[v] = lane_in ? val : 0.f;
+        }
+    }
+};
+
 // Mean and rstd of one row from its lanes' chunks (lanes past the row hold zeros).
 template <typename T, int TPR>
 __device__ __forceinline__ void ln_stats_flat(const RowRegs<T, MODE_ALIGNED, 1>& xr, bool lane_in,
@@ -636,12 +676,12 @@ ln_fwd_flat_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const 
                    float eps, T* __restrict__ y, float* __restrict__ mean_out,
                    float* __restrict__ rstd_out, Geom g) {
     constexpr int V = Elems<T, MODE_ALIGNED>::value;
-    RowCtx<T, MODE_ALIGNED, 1, 1> c(g);
+    const FlatCtx<T, PT, TPR> c(g);
     float ga[V], be[V];
-    load_param_or<T, PT, MODE_ALIGNED, 1>(gamma, 1.f, g.N, c.cm, ga);
-    load_param_or<T, PT, MODE_ALIGNED, 1>(beta, 0.f, g.N, c.cm, be);
-    const bool lane_in = c.cm.any[0];
-    const int64_t col = lane_in ? c.cm.col0[0] : 0;
+    c.param(gamma, 1.f, ga);
+    c.param(beta, 0.f, be);
+    const bool lane_in = c.lane_in;
+    const int64_t col = c.col;
     for (int64_t tile = c.t_begin; tile < c.t_end; tile += c.t_step) {
         const int64_t row = tile * c.rows_per_tile + c.slot;
         const bool ok = row < g.M;
@@ -669,11 +709,11 @@ ln_bwd_flat_kernel(const T* __restrict__ x, const T* __restrict__ dy, const floa
                    T* __restrict__ dx, float* __restrict__ ws, Geom g) {
     constexpr int V = Elems<T, MODE_ALIGNED>::value;
     extern __shared__ float part[];
-    RowCtx<T, MODE_ALIGNED, 1, 1> c(g);
+    const FlatCtx<T, PT, TPR> c(g);
     float ga[V];
-    load_param_or<T, PT, MODE_ALIGNED, 1>(gamma, 1.f, g.N, c.cm, ga);
-    const bool lane_in = c.cm.any[0];
-    const int64_t col = lane_in ? c.cm.col0[0] : 0;
+    c.param(gamma, 1.f, ga);
+    const bool lane_in = c.lane_in;
+    const int64_t col = c.col;
     float acc_g[V], acc_b[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc_g[v] = acc_b[v] = 0.f;
