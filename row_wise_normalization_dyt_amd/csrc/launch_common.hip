@@ -242,9 +242,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     if (p.block > maxb) return false;
     const int64_t rows_per_tile = (int64_t)p.rpp * p.rt;
     p.ntiles = (M + rows_per_tile - 1) / rows_per_tile;
-    if (backward && p.rpp > 1) {   // LDS for combining the row slots' partials
+    if (backward && (p.rpp > 1 || p.flat)) {   // LDS for combining the row slots' partials
         int64_t e = (int64_t)p.cpt * v_elems * p.block;
         if (p.mode == MODE_SHIFTED && N > e) e = N;
+        if (p.flat) e *= 2;   // the flat backward combines dgamma and dbeta together
         p.lds_bytes = (size_t)e * sizeof(float);
     }
     // Workgroups of this kernel that fit on a CU at once: every workgroup of a persistent grid

@@ -652,6 +652,49 @@ struct FlatCtx {
     }
 };
 
+// Both LayerNorm partial rows of a flat workgroup (dgamma at out_g, dbeta at out_b, column
+// stride cs) in one combine: the two gradients' butterflies interleave and share one LDS round,
+// so the workgroup's tail pays the latency once.  The order is write_partial's for narrow rows:
+// an xor butterfly over the wave's row slots, then the waves' sums in wave order.
+template <typename T, int TPR>
+__device__ __forceinline__ void write_partial_pair(float* __restrict__ out_g, float* __restrict__ out_b,
+                                                   int64_t cs, const float* acc_g, const float* acc_b,
+                                                   int lane, bool lane_in, int64_t col, float* part) {
+    constexpr int V = Elems<T, MODE_ALIGNED>::value;
+    constexpr int E = 2 * V;
+    const int nb = blockDim.x;
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        v[e] = acc_g[e];
+        v[V + e] = acc_b[e];
+    }
+    if constexpr (TPR < 64) {
+        const int wl = nb < 64 ? nb : 64;
+        for (int off = TPR; off < wl; off <<= 1) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] += __shfl_xor(v[e], off, 64);
+        }
+    }
+    const int nw = (nb + 63) >> 6;
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) < TPR) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) part[(wave * TPR + lane) * E + e] = v[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < TPR && lane_in) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float sum = part[lane * E + e];
+            for (int w = 1; w < nw; ++w) sum += part[(w * TPR + lane) * E + e];
+            if (e < V) out_g[(col + e) * cs] = sum;
+            else out_b[(col + e - V) * cs] = sum;
+        }
+    }
+}
+
 // Mean and rstd of one row from its lanes' chunks (lanes past the row hold zeros).
 template <typename T, int TPR>
 __device__ __forceinline__ void ln_stats_flat(const RowRegs<T, MODE_ALIGNED, 1>& xr, bool lane_in,
@@ -758,8 +801,8 @@ ln_bwd_flat_kernel(const T* __restrict__ x, const T* __restrict__ dy, const floa
     }
     if constexpr (PG) {
         float* out = ws + c.wg * g.ws_rs;
-        write_partial<T, MODE_ALIGNED, 1>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
-        write_partial<T, MODE_ALIGNED, 1>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
+        write_partial_pair<T, TPR>(out, out + g.N * g.ws_cs, g.ws_cs, acc_g, acc_b, c.lane, c.lane_in,
+                                   c.col, part);
     }
 }
 
