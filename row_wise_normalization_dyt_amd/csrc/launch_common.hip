@@ -220,6 +220,13 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         if (prefetch >= 0) p.pf = (prefetch == 2 && !(one && p.mode != MODE_SCALAR)) ? 1 : prefetch;
         else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
         else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
+        else if (layer == LAYER_RMS && p.mode == MODE_ALIGNED && p.tpr >= 128 &&
+                 (p.tpr >= 1024 || M <= (int64_t)32 * cus * std::max(1, wide_block / p.tpr)))
+            // Aligned RMSNorm backwards of two or more waves per row, pipelined (measured): 16-wave
+            // rows (65536 x 16384 bf16, 1211 -> 1119 us) and shapes with at most ~32 row tiles per
+            // CU (16384 x 2048 and 8192 x 4096 bf16, 3-6% faster); with more tiles per CU, as at
+            // 65536 x 4096..8192, it measured 3-7% slower.
+            p.pf = 1;
         else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
     }
     // Narrow aligned LayerNorm rows, one chunk and one row per thread, take the flat kernels
