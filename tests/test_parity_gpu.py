@@ -45,8 +45,8 @@ def test_small_shapes_span_tiles_and_ragged_tails(layer, xdt, pdt):
     tol.assert_reports(reps)
 
 
-EDGE_N = [1, 2, 3, 7, 15, 16, 17, 24, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257,
-          1023, 1024, 1025, 2048, 2049]
+EDGE_N = [1, 2, 3, 4, 7, 8, 15, 16, 17, 24, 31, 32, 33, 63, 64, 65, 127, 128, 129, 130, 255, 256, 257,
+          512, 1023, 1024, 1025, 2048, 2049]
 
 
 @pytest.mark.parametrize("xdt,pdt", DTYPE_PAIRS)
