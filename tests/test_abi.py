@@ -186,6 +186,26 @@ def test_plan_uses_narrow_tiles_for_narrow_rows():
     assert p["grid"] == 1 and p["ntiles"] == 1
 
 
+@pytest.mark.parametrize("backward", [False, True])
+def test_flat_plans(backward):
+    """The flat kernels take exactly the narrow aligned LayerNorm plans with one chunk and one
+    row per thread (group sizes 1..64 lanes, no pipelining, at most 256 threads); every other
+    plan, and every other layer, keeps the general kernels."""
+    for dtype, V in ((torch.float32, 4), (torch.bfloat16, 8), (torch.float16, 8)):
+        for N in (V, 2 * V, 24 if V == 4 else 32, 16 * V, 64 * V, 64 * V + V, 1025):
+            for mis in (0, 2 if V == 8 else 4):
+                for layer in ("dyt", "layernorm", "rmsnorm"):
+                    p = rwn.plan(layer, backward, 4099, N, dtype, misalign_bytes=mis, cus=256)
+                    want = (layer == "layernorm" and p["mode"] == 0 and p["cpt"] == 1 and p["rt"] == 1
+                            and p["tpr"] <= 64 and p["ncb"] == 1)
+                    assert p["flat"] == int(want), (layer, N, mis, p)
+                    if p["flat"]:
+                        assert N % V == 0 and mis == 0 and p["prefetch"] == 0 and p["block"] <= 256, p
+                        assert p["tpr"] in (1, 2, 4, 8, 16, 32, 64) and p["block"] == p["tpr"] * p["rpp"], p
+    p = rwn.plan("layernorm", backward, 401408, 24, torch.float32, cus=256)
+    assert p["flat"] == 1 and p["xcd_remap"] == 0
+
+
 def test_plan_is_deterministic():
     a = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
     b = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
@@ -222,7 +242,7 @@ print("BAD", bad)
 
 @pytest.mark.parametrize("env", ["RWN_WIDE_BLOCK=1024", "RWN_WIDE_BLOCK=64", "RWN_FWD_RT=4", "RWN_BWD_RT=2",
                                  "RWN_MIN_WAVES=32", "RWN_WG_PER_CU=3", "RWN_BLOCKED_K=3", "RWN_PREFETCH=1",
-                                 "RWN_PREFETCH=0", "RWN_X=0"])
+                                 "RWN_PREFETCH=0", "RWN_X=0", "RWN_FLAT=0"])
 def test_plans_respect_kernel_launch_bounds_under_tuning_overrides(env):
     """Every plan's workgroup fits the launch bound its kernel was compiled for, also with the
     tuning overrides set (a plan over the bound would fail to launch)."""
