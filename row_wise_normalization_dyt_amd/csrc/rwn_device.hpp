@@ -102,11 +102,10 @@ struct ColMap {
     bool any[CPT];      // at least one column inside [0, N)
     int shift;          // SHIFTED: s of this thread's rows
     // SHIFTED only (fixed per thread, so computed once): the bits of each 32-bit word of chunk
-    // k that hold elements inside the row, and 1.0 / 0.0 per element inside / outside it.
-    // Kept as vector registers, they turn the per-element masks of the row loop into one AND
-    // per word and one multiply-add per element, with no per-element compares.
+    // k that hold elements inside the row.  Kept as vector registers, they turn the masks of the
+    // row loop into one AND per loaded word, and an element's own mask is derived from them
+    // where needed (row_mask, in_row) with shifts instead of per-element compares.
     uint32_t keep[CPT][4];
-    float inrow[CPT][V];
 
     __device__ __forceinline__ void init(int lane, int tpr, int64_t N, int s, int chunk_base = 0) {
         shift = s;
@@ -123,7 +122,6 @@ struct ColMap {
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
                     const bool in = j0 + v >= 0 && (int64_t)(j0 + v) < N;
-                    inrow[k][v] = in ? 1.f : 0.f;
                     if (in) {
                         if constexpr (sizeof(T) == 4) keep[k][v] = 0xFFFFFFFFu;
                         else keep[k][v >> 1] |= (v & 1) ? 0xFFFF0000u : 0x0000FFFFu;
@@ -132,6 +130,12 @@ struct ColMap {
             }
         }
     }
+    // SHIFTED: all ones for element v of chunk k inside the row, zero outside.
+    __device__ __forceinline__ uint32_t row_mask(int k, int v) const {
+        if constexpr (sizeof(T) == 4) return keep[k][v];
+        else return (uint32_t)((int32_t)((v & 1) ? keep[k][v >> 1] : keep[k][v >> 1] << 16) >> 31);
+    }
+    __device__ __forceinline__ bool in_row(int k, int v) const { return row_mask(k, v) != 0u; }
     __device__ __forceinline__ bool valid(int k, int v, int64_t N) const {
         if (MODE == MODE_SHIFTED) {
             int j = col0[k] + v;
@@ -383,7 +387,7 @@ __device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int6
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
-            if (cm.inrow[k][v] != 0.f) rp[v] = from_f32<T>(o[v]);
+            if (cm.in_row(k, v)) rp[v] = from_f32<T>(o[v]);
     }
 }
 

@@ -419,8 +419,9 @@ __device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 if constexpr (MODE == MODE_SHIFTED) {
-                    // elements outside the row read as 0, so d is exactly 0 for them
-                    const float d = __builtin_fmaf(-mu[u], cm.inrow[k][v], xr[u].get(k, v));
+                    // d masked to exactly 0 for elements outside the row
+                    const float d = __builtin_bit_cast(
+                        float, __builtin_bit_cast(uint32_t, xr[u].get(k, v) - mu[u]) & cm.row_mask(k, v));
                     a = __builtin_fmaf(d, d, a);
                 } else {
                     const float d = xr[u].get(k, v) - mu[u];
