@@ -890,8 +890,16 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     tile_loop<PF, In>(c, fetch, body);
 }
 
+// Resident waves per SIMD the RMSNorm backward is compiled for: the SHIFTED one-chunk shape
+// (N = 1025 bf16) fits five when it keeps to 96 VGPRs (one more register costs a wave:
+// 87.8 vs 90.8 us); other shapes are left to the compiler.
+template <int MODE, int CPT> struct RmsBwdWaves {
+    static constexpr int value = (MODE == MODE_SHIFTED && CPT == 1) ? 5 : 1;
+};
+
 template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR, int PG>
-__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value),
+                               amdgpu_waves_per_eu(RmsBwdWaves<MODE, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                const PT* __restrict__ weight, float eps, T* __restrict__ dx,
                float* __restrict__ ws, Geom g) {
