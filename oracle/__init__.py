@@ -82,7 +82,7 @@ def _bind(lib):
     dp = ctypes.c_void_p
     lib.oracle_dyt_fwd.argtypes = [i64, i64, vp, ci, cd, vp, vp, ci, dp, dp]
     lib.oracle_dyt_bwd.argtypes = [i64, i64, vp, vp, ci, cd, vp, ci, dp, dp, dp, dp, dp, dp, dp, dp]
-    lib.oracle_layernorm_fwd.argtypes = [i64, i64, vp, ci, vp, vp, ci, cd, dp, dp, dp, dp]
+    lib.oracle_layernorm_fwd.argtypes = [i64, i64, vp, ci, vp, vp, ci, cd, dp, dp, dp, dp, dp, dp]
     lib.oracle_layernorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp, dp]
     lib.oracle_rmsnorm_fwd.argtypes = [i64, i64, vp, ci, vp, ci, cd, dp, dp, dp, dp]
     lib.oracle_rmsnorm_bwd.argtypes = [i64, i64, vp, vp, ci, vp, ci, cd, dp, dp, dp, dp, dp]
@@ -178,11 +178,11 @@ def layernorm_fwd(x, gamma, beta, eps: float) -> Dict[str, np.ndarray]:
     lib = _load()
     x, gamma, beta = _host(x, "x"), _host(gamma, "gamma"), _host(beta, "beta")
     M, N = x.shape
-    y, ys, mu, rs = _out((M, N)), _out((M, N)), _out(M), _out(M)
+    y, ys, mu, rs, ms, vs = _out((M, N)), _out((M, N)), _out(M), _out(M), _out(M), _out(M)
     _check(lib.oracle_layernorm_fwd(M, N, x.data_ptr(), _DT[x.dtype], gamma.data_ptr(),
                                     beta.data_ptr(), _DT[gamma.dtype], float(eps), _p(y), _p(ys),
-                                    _p(mu), _p(rs)), "oracle_layernorm_fwd")
-    return {"y": y, "y_scale": ys, "mean": mu, "rstd": rs}
+                                    _p(mu), _p(rs), _p(ms), _p(vs)), "oracle_layernorm_fwd")
+    return {"y": y, "y_scale": ys, "mean": mu, "rstd": rs, "mean_scale": ms, "rstd_scale": vs}
 
 
 def layernorm_bwd(x, dy, gamma, eps: float, want_dx: bool = True) -> Dict[str, np.ndarray]:

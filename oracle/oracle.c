@@ -201,10 +201,12 @@ typedef struct {
     double alpha;
 } dyt_ctx;
 
-/* Column terms of row i: [dy*t (N) | dy (N) | dy*gamma*x*sech^2 summed over the row (1)]. */
+/* Column terms of row i: [dy*t (N) | dy (N) | dy*gamma*x*sech^2 summed over the row (1) |
+ * the magnitudes of those dalpha terms summed over the row (1)].  dalpha is one sum over all
+ * M * N products, so its magnitude sum adds |term| over every (i, j), not |row sum| per row. */
 static void dyt_bwd_terms(const void* vctx, int64_t i, double* terms) {
     const dyt_ctx* c = (const dyt_ctx*)vctx;
-    double da = 0.0;
+    double da = 0.0, daa = 0.0;
     for (int64_t j = 0; j < c->N; ++j) {
         double xv = load_elem(c->x, c->xdt, i * c->N + j);
         double g = load_elem(c->dy, c->xdt, i * c->N + j);
@@ -212,9 +214,12 @@ static void dyt_bwd_terms(const void* vctx, int64_t i, double* terms) {
         terms[j] = g * tanh(z);
         terms[c->N + j] = g;
         double s = sech2(z);
-        da += g * load_elem(c->gamma, c->pdt, j) * xv * s;
+        double t = g * load_elem(c->gamma, c->pdt, j) * xv * s;
+        da += t;
+        daa += fabs(t);
     }
     terms[2 * c->N] = da;
+    terms[2 * c->N + 1] = daa;
 }
 
 /* [DyT] Summary.  With t = tanh(alpha x) and s = sech^2(alpha x):
@@ -242,7 +247,7 @@ int oracle_dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
     }
     if (dgamma || dbeta || dalpha || dgamma_scale || dbeta_scale || dalpha_scale) {
         dyt_ctx c = {N, x, dy, gamma, xdt, pdt, alpha};
-        int64_t nc = 2 * N + 1;
+        int64_t nc = 2 * N + 2;
         double* s = (double*)malloc((size_t)nc * sizeof(double));
         double* a = (double*)malloc((size_t)nc * sizeof(double));
         if (!s || !a || column_sums(&c, dyt_bwd_terms, M, nc, s, a) != 0) {
@@ -256,7 +261,7 @@ int oracle_dyt_bwd(int64_t M, int64_t N, const void* x, const void* dy, int xdt,
             if (dbeta_scale) dbeta_scale[j] = a[N + j];
         }
         if (dalpha) *dalpha = s[2 * N];
-        if (dalpha_scale) *dalpha_scale = a[2 * N];
+        if (dalpha_scale) *dalpha_scale = s[2 * N + 1];
         free(s); free(a);
     }
     return 0;
@@ -290,10 +295,14 @@ static double row_abs_mean(const void* x, int xdt, int64_t i, int64_t N) {
 /* [LN] (torch.nn.LayerNorm reading).  xhat = (x - mu) * rstd; y = xhat * gamma + beta.
  * y_scale sums the magnitudes of every term of y expanded through mu = sum_j x_j / N:
  * rstd * |gamma| * (|x| + sum_j |x_j| / N) + |beta|.  mean/rstd (may be NULL) receive mu and
- * rstd. */
+ * rstd; mean_scale the magnitude sum of mu (sum_j |x_j| / N); rstd_scale bounds rstd's error
+ * through that of var + eps: with V = sum_j (|x_j| + sum_k |x_k| / N)^2 / N, the magnitude sum
+ * of the biased variance expanded through mu, rstd_scale = rstd * (V + eps) / (var + eps), twice
+ * the first-order propagation (d rstd / rstd = -d(var + eps) / (2 (var + eps))).  Both may be
+ * NULL. */
 int oracle_layernorm_fwd(int64_t M, int64_t N, const void* x, int xdt, const void* gamma,
                          const void* beta, int pdt, double eps, double* y, double* y_scale,
-                         double* mean, double* rstd) {
+                         double* mean, double* rstd, double* mean_scale, double* rstd_scale) {
     if (M < 0 || N < 1) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; ++i) {
@@ -302,6 +311,16 @@ int oracle_layernorm_fwd(int64_t M, int64_t N, const void* x, int xdt, const voi
         if (mean) mean[i] = mu;
         if (rstd) rstd[i] = r;
         const double am = row_abs_mean(x, xdt, i, N);
+        if (mean_scale) mean_scale[i] = am;
+        if (rstd_scale) {
+            double vs = 0.0;
+            for (int64_t j = 0; j < N; ++j) {
+                double m = fabs(load_elem(x, xdt, i * N + j)) + am;
+                vs += m * m;
+            }
+            vs /= (double)N;
+            rstd_scale[i] = r * (vs + eps) * (r * r);   /* r^2 = 1 / (var + eps) */
+        }
         for (int64_t j = 0; j < N; ++j) {
             double xv = load_elem(x, xdt, i * N + j);
             double xh = (xv - mu) * r;
