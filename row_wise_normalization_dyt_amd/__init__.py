@@ -102,20 +102,55 @@ def workspace_size(layer: str, M: int, N: int, dtype: torch.dtype, device=None) 
     return int(out.value)
 
 
-def _workspace(layer: str, M: int, N: int, dtype, dev) -> torch.Tensor:
+def _workspace(layer: str, M: int, N: int, dtype, dev, given: Optional[torch.Tensor] = None) -> torch.Tensor:
     n = workspace_size(layer, M, N, dtype, dev)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    if given is None:
+        return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    if given.device != dev or not given.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    if given.numel() * given.element_size() < n:
+        raise ValueError(f"workspace has {given.numel() * given.element_size()} bytes, {n} needed")
+    return given
+
+
+def _ws_bytes(ws: Optional[torch.Tensor]) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _out_rows(given: Optional[torch.Tensor], x2: torch.Tensor, name: str) -> torch.Tensor:
+    """An [M, N] output: a fresh tensor laid out like x2, or the caller's buffer (contiguous, x's
+    dtype and device, M * N elements, the same address as x2 modulo 16 bytes)."""
+    if given is None:
+        return _like(x2)
+    if given.device != x2.device or given.dtype != x2.dtype:
+        raise ValueError(f"{name} must be a {x2.dtype} tensor on {x2.device}")
+    if not given.is_contiguous() or given.numel() != x2.numel():
+        raise ValueError(f"{name} must be contiguous with {x2.numel()} elements")
+    if given.data_ptr() % 16 != x2.data_ptr() % 16:
+        raise ValueError(f"{name} must share x's address modulo 16 bytes")
+    return given.view(x2.shape)
+
+
+def _out_vec(given: Optional[torch.Tensor], n: int, dtype, dev, name: str) -> torch.Tensor:
+    """A length-n output vector: fresh, or the caller's contiguous buffer of that dtype."""
+    if given is None:
+        return torch.empty(n, dtype=dtype, device=dev)
+    if given.device != dev or given.dtype != dtype or not given.is_contiguous() or given.numel() != n:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} elements on {dev}")
+    return given.view(n)
 
 
 # ------------------------------------------------------------------------------------ DyT
 
-def dyt_fwd(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor) -> torch.Tensor:
-    """y = gamma * tanh(alpha * x) + beta over the last dimension; y has x's shape and dtype."""
+def dyt_fwd(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, *,
+            y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = gamma * tanh(alpha * x) + beta over the last dimension; y has x's shape and dtype.
+    y=: an output buffer to write instead of a fresh tensor."""
     lib = _L()
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     alpha, gamma, beta = _vec(alpha, 1, "alpha", x2.device), _vec(gamma, N, "gamma", x2.device), _vec(beta, N, "beta", x2.device)
-    y = _like(x2)
+    y = _out_rows(y, x2, "y")
     with torch.cuda.device(x2.device):
         _lib.check(lib, "dyt_fwd", lib.dyt_fwd(M, N, _ptr(x2), _dt(x2, "x"), _ptr(alpha), _ptr(gamma), _ptr(beta),
                                                _param_dtype(alpha, gamma, beta), _ptr(y), _stream(x2.device)))
@@ -123,8 +158,11 @@ def dyt_fwd(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: tor
 
 
 def dyt_bwd(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor,
-            need_param_grads: bool = True) -> Tuple[torch.Tensor, ...]:
-    """Returns (dx, dalpha [1], dgamma [N], dbeta [N]); gradients in the parameters' dtype."""
+            need_param_grads: bool = True, *, dx: Optional[torch.Tensor] = None,
+            dalpha: Optional[torch.Tensor] = None, dgamma: Optional[torch.Tensor] = None,
+            dbeta: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
+    """Returns (dx, dalpha [1], dgamma [N], dbeta [N]); gradients in the parameters' dtype.
+    dx=, dalpha=, dgamma=, dbeta=, workspace=: buffers to use instead of fresh tensors."""
     lib = _L()
     x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
@@ -133,14 +171,14 @@ def dyt_bwd(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch
     M, N = x2.shape
     alpha, gamma = _vec(alpha, 1, "alpha", x2.device), _vec(gamma, N, "gamma", x2.device)
     pdt = _param_dtype(alpha, gamma)
-    dx = _like(x2)
-    da = torch.empty(1, dtype=gamma.dtype, device=x2.device) if need_param_grads else None
-    dg = torch.empty(N, dtype=gamma.dtype, device=x2.device) if need_param_grads else None
-    db = torch.empty(N, dtype=gamma.dtype, device=x2.device) if need_param_grads else None
+    dx = _out_rows(dx, x2, "dx")
+    da = _out_vec(dalpha, 1, gamma.dtype, x2.device, "dalpha") if need_param_grads else None
+    dg = _out_vec(dgamma, N, gamma.dtype, x2.device, "dgamma") if need_param_grads else None
+    db = _out_vec(dbeta, N, gamma.dtype, x2.device, "dbeta") if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("dyt", M, N, x2.dtype, x2.device) if need_param_grads else None
+        ws = _workspace("dyt", M, N, x2.dtype, x2.device, workspace) if need_param_grads else None
         _lib.check(lib, "dyt_bwd", lib.dyt_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(alpha), _ptr(gamma), pdt,
-                                               _ptr(dx), _ptr(da), _ptr(dg), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
+                                               _ptr(dx), _ptr(da), _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),
                                                _stream(x2.device)))
     return dx.reshape(x.shape), da, dg, db
 
@@ -148,16 +186,18 @@ def dyt_bwd(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch
 # ------------------------------------------------------------------------------ LayerNorm
 
 def layernorm_fwd(x: torch.Tensor, gamma: Optional[torch.Tensor], beta: Optional[torch.Tensor], eps: float,
-                  want_stats: bool = True):
-    """Returns (y, mean [M] float32, rstd [M] float32); mean/rstd are None if not wanted."""
+                  want_stats: bool = True, *, y: Optional[torch.Tensor] = None,
+                  mean: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None):
+    """Returns (y, mean [M] float32, rstd [M] float32); mean/rstd are None if not wanted.
+    y=, mean=, rstd=: buffers to write instead of fresh tensors."""
     lib = _L()
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     gamma, beta = _vec(gamma, N, "gamma", x2.device), _vec(beta, N, "beta", x2.device)
     pdt = _param_dtype(gamma, beta) if (gamma is not None or beta is not None) else _lib.RWN_F32
-    y = _like(x2)
-    mean = torch.empty(M, dtype=torch.float32, device=x2.device) if want_stats else None
-    rstd = torch.empty(M, dtype=torch.float32, device=x2.device) if want_stats else None
+    y = _out_rows(y, x2, "y")
+    mean = _out_vec(mean, M, torch.float32, x2.device, "mean") if want_stats else None
+    rstd = _out_vec(rstd, M, torch.float32, x2.device, "rstd") if want_stats else None
     with torch.cuda.device(x2.device):
         _lib.check(lib, "layernorm_fwd", lib.layernorm_fwd(M, N, _ptr(x2), _dt(x2, "x"), _ptr(gamma), _ptr(beta), pdt,
                                                            float(eps), _ptr(y), _ptr(mean), _ptr(rstd),
@@ -167,8 +207,11 @@ def layernorm_fwd(x: torch.Tensor, gamma: Optional[torch.Tensor], beta: Optional
 
 def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor], rstd: Optional[torch.Tensor],
                   gamma: Optional[torch.Tensor], eps: float, param_dtype: Optional[torch.dtype] = None,
-                  need_param_grads: bool = True):
-    """Returns (dx, dgamma, dbeta).  mean/rstd None: recomputed from x."""
+                  need_param_grads: bool = True, *, dx: Optional[torch.Tensor] = None,
+                  dgamma: Optional[torch.Tensor] = None, dbeta: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Returns (dx, dgamma, dbeta).  mean/rstd None: recomputed from x.
+    dx=, dgamma=, dbeta=, workspace=: buffers to use instead of fresh tensors."""
     lib = _L()
     x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
@@ -182,14 +225,14 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
     for t, nm in ((mean, "mean"), (rstd, "rstd")):
         if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{nm} must be float32")
-    dx = _like(x2)
-    dg = torch.empty(N, dtype=pdtype, device=x2.device) if need_param_grads else None
-    db = torch.empty(N, dtype=pdtype, device=x2.device) if need_param_grads else None
+    dx = _out_rows(dx, x2, "dx")
+    dg = _out_vec(dgamma, N, pdtype, x2.device, "dgamma") if need_param_grads else None
+    db = _out_vec(dbeta, N, pdtype, x2.device, "dbeta") if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("layernorm", M, N, x2.dtype, x2.device) if need_param_grads else None
+        ws = _workspace("layernorm", M, N, x2.dtype, x2.device, workspace) if need_param_grads else None
         _lib.check(lib, "layernorm_bwd", lib.layernorm_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(mean),
                                                            _ptr(rstd), _ptr(gamma), _DT[pdtype], float(eps),
-                                                           _ptr(dx), _ptr(dg), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
+                                                           _ptr(dx), _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),
                                                            _stream(x2.device)))
     return dx.reshape(x.shape), dg, db
 
@@ -206,15 +249,16 @@ def _form(form: str) -> int:
 
 
 def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: bool = True,
-                form: str = "cast_then_weight"):
+                form: str = "cast_then_weight", *, y: Optional[torch.Tensor] = None,
+                rstd: Optional[torch.Tensor] = None):
     """Returns (y, rstd [M] float32 or None); y keeps x's dtype.  form: "cast_then_weight"
-    (Llama), "weight_then_cast" or "one_plus_weight" (Gemma)."""
+    (Llama), "weight_then_cast" or "one_plus_weight" (Gemma).  y=, rstd=: buffers to write."""
     lib = _L()
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     weight = _vec(weight, N, "weight", x2.device)
-    y = _like(x2)
-    rstd = torch.empty(M, dtype=torch.float32, device=x2.device) if want_stats else None
+    y = _out_rows(y, x2, "y")
+    rstd = _out_vec(rstd, M, torch.float32, x2.device, "rstd") if want_stats else None
     with torch.cuda.device(x2.device):
         _lib.check(lib, "rmsnorm_fwd_form", lib.rmsnorm_fwd_form(M, N, _ptr(x2), _dt(x2, "x"), _ptr(weight),
                                                                  _dt(weight, "weight"), float(eps), _form(form),
@@ -223,8 +267,11 @@ def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: b
 
 
 def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor], weight: torch.Tensor, eps: float,
-                need_param_grads: bool = True, form: str = "cast_then_weight"):
-    """Returns (dx, dweight).  rstd None: recomputed from x."""
+                need_param_grads: bool = True, form: str = "cast_then_weight", *,
+                dx: Optional[torch.Tensor] = None, dweight: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Returns (dx, dweight).  rstd None: recomputed from x.  dx=, dweight=, workspace=: buffers
+    to use instead of fresh tensors."""
     lib = _L()
     x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
@@ -235,14 +282,14 @@ def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor],
     rstd = _vec(rstd, M, "rstd", x2.device) if rstd is not None else None
     if rstd is not None and rstd.dtype != torch.float32:
         raise TypeError("rstd must be float32")
-    dx = _like(x2)
-    dw = torch.empty(N, dtype=weight.dtype, device=x2.device) if need_param_grads else None
+    dx = _out_rows(dx, x2, "dx")
+    dw = _out_vec(dweight, N, weight.dtype, x2.device, "dweight") if need_param_grads else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("rmsnorm", M, N, x2.dtype, x2.device) if need_param_grads else None
+        ws = _workspace("rmsnorm", M, N, x2.dtype, x2.device, workspace) if need_param_grads else None
         _lib.check(lib, "rmsnorm_bwd_form", lib.rmsnorm_bwd_form(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(rstd),
                                                                  _ptr(weight), _dt(weight, "weight"), float(eps),
                                                                  _form(form), _ptr(dx), _ptr(dw), _ptr(ws),
-                                                                 0 if ws is None else ws.numel(), _stream(x2.device)))
+                                                                 _ws_bytes(ws), _stream(x2.device)))
     return dx.reshape(x.shape), dw
 
 

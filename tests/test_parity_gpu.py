@@ -201,12 +201,14 @@ def test_empty_input(layer):
 
 @pytest.mark.parametrize("layer", LAYERS)
 def test_backward_is_bitwise_reproducible(layer):
+    """Two runs on the same inputs, each into fresh NaN-poisoned outputs and workspace, give the
+    same bits everywhere (parameter gradients included)."""
     for (M, N, xdt) in [(401408, 24, "f32"), (8192, 128, "bf16"), (4099, 2048, "bf16"), (2049, 1025, "bf16")]:
         wl = workloads.small(layer, M, N, xdt, "f32", seed=1)
         _banner(wl, "determinism")
         inp = {k: v.to(DEV) for k, v in workloads.make_inputs(wl, DEV).items()}
-        a = gc.gpu_run(layer, inp, wl.eps)
-        b = gc.gpu_run(layer, inp, wl.eps)
+        a = gc.gpu_run(layer, inp, wl.eps, poison=True)
+        b = gc.gpu_run(layer, inp, wl.eps, poison=True)
         for k in a:
             if a[k] is not None:
                 assert torch.equal(a[k].view(torch.uint8) if a[k].dtype == torch.bfloat16 else a[k],
@@ -270,15 +272,43 @@ def test_dx_only_backward_matches_full_backward(layer):
         assert torch.equal(only[0].view(torch.uint8), full[0].view(torch.uint8)), wl.name
 
 
+# Workloads compared on every element of y, dx and the statistics (the oracle streams row
+# chunks); the others (the 134M- to 1G-element ones) are compared on whole launch tiles.
+FULL_ROWS = {n for n, w in workloads.WORKLOADS.items() if w.M * w.N <= (40 << 20)}
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(name):
-    """Every workload at its real size, in the launch configuration the benchmark times:
-    y/dx/stats on sampled rows (first, last, tile boundaries, random), parameter gradients
-    over all M rows."""
+    """Every workload at its real size, in the launch configuration the benchmark times, with
+    NaN-poisoned outputs and workspace: y/dx/stats on every row (workloads up to 40M elements)
+    or on whole tiles of 16 workgroups spread over the forward and backward grids (first, middle
+    and last tile of each, and the grid's last tile); parameter gradients over all M rows."""
     wl = workloads.WORKLOADS[name]
-    _banner(name)
-    rows = gc.sample_rows(wl.M, k=24)
-    reps = gc.check_workload(wl, DEV, rows=rows, on_gpu_inputs=True)
+    if name in FULL_ROWS:
+        _banner(name, "all rows")
+        reps = gc.check_full_rows(wl, DEV)
+    else:
+        rows = gc.tile_rows(wl)
+        _banner(name, "whole tiles", len(rows), "rows")
+        reps = gc.check_workload(wl, DEV, rows=rows, on_gpu_inputs=True)
+    for r in reps:
+        print("  ", r, flush=True)
+    tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("layer,M,N,xdt,pdt", [("dyt", 300000, 24, "bf16", "f32"), ("dyt", 300000, 128, "bf16", "f32"),
+                                               ("rmsnorm", 40000, 2048, "bf16", "bf16"),
+                                               ("layernorm", 300000, 24, "f32", "f32"),
+                                               ("layernorm", 40000, 1025, "bf16", "f32")])
+def test_multi_tile_workgroups_all_rows(layer, M, N, xdt, pdt):
+    """Shapes where every workgroup of the persistent grids walks several tiles, so the
+    pipelined tile loops rotate through all of their buffers; every element compared."""
+    wl = workloads.small(layer, M, N, xdt, pdt, seed=M + N)
+    pf = rwn.plan(layer, False, M, N, gc.DT[xdt], param_dtype=gc.DT[pdt])
+    pb = rwn.plan(layer, True, M, N, gc.DT[xdt])
+    assert pf["ntiles"] >= 4 * pf["grid"] // pf["ncb"] or pb["ntiles"] >= 4 * pb["grid"] // pb["ncb"]
+    _banner(wl, "multi-tile", pf["ntiles"] * pf["ncb"] / pf["grid"], pb["ntiles"] * pb["ncb"] / pb["grid"])
+    reps = gc.check_full_rows(wl, DEV)
     tol.assert_reports(reps)
 
 

@@ -28,9 +28,10 @@ def ulp(v: np.ndarray, dtype: torch.dtype) -> np.ndarray:
     """Spacing of dtype's values at |v| (binade-based; subnormal spacing below the normal range)."""
     a = np.abs(np.asarray(v, dtype=np.float64))
     mant, emin = {torch.bfloat16: (7, -126), torch.float16: (10, -14)}.get(dtype, (23, -126))
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(e, emin)
-    return np.where(np.isfinite(a), np.exp2(e - mant), np.inf)
+    # frexp: a = f * 2^k with f in [0.5, 1), so the binade exponent is k - 1
+    _, k = np.frexp(np.where(np.isfinite(a) & (a > 0), a, 1.0))
+    e = np.maximum(k.astype(np.int64) - 1, emin)
+    return np.where(np.isfinite(a), np.ldexp(1.0, e - mant), np.inf)
 
 
 @dataclasses.dataclass
@@ -104,6 +105,16 @@ def compare_param(name: str, gpu: torch.Tensor, exact: np.ndarray, abs_sum: np.n
     return Report(name, int(err.size), bad, float(np.max(ratio)) if ratio.size else 0.0,
                   float(np.max(err / u)) if err.size else 0.0,
                   float(np.mean(err <= u)) if err.size else 1.0, worst)
+
+
+def merge(reports) -> Report:
+    """One report over the union of several reports' elements (e.g. row chunks of a tensor)."""
+    reports = list(reports)
+    n = sum(r.n for r in reports)
+    worst = max(reports, key=lambda r: r.max_ratio)
+    return Report(reports[0].name, n, sum(r.bad for r in reports), max(r.max_ratio for r in reports),
+                  max(r.max_ulp for r in reports),
+                  sum(r.within_1ulp * r.n for r in reports) / n if n else 1.0, worst.worst)
 
 
 def assert_reports(reports) -> None:
