@@ -113,6 +113,21 @@ rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy, rw
 
 rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes);
 
+/* layernorm_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc).  The partial rows go to a static device array of 32 MiB that the library holds on
+ * each device it runs on until the process ends; nothing is allocated or freed by the call.
+ * Arguments, results and errors are layernorm_bwd's, and so are the kernels: results are bitwise
+ * those of layernorm_bwd with a workspace.  A shape whose partial rows need more than 32 MiB
+ * (layernorm_bwd_workspace_size reports the need) returns RWN_ERR_UNSUPPORTED before anything
+ * is launched.  Every call on a device shares that device's array, and nothing in it needs to
+ * start at zero (each call writes every partial it reads), but calls that overlap in time on
+ * one device -- concurrent streams, or host threads -- race on it: serialize them. */
+rwn_status layernorm_bwd_noalloc(int64_t M, int64_t N, const void* x, const void* dy,
+                                 rwn_dtype x_dtype, const float* mean, const float* rstd,
+                                 const void* gamma, rwn_dtype param_dtype, float eps, void* dx,
+                                 void* dgamma, void* dbeta, void* stream);
+
 /* ------------------------------------------------------------------------------ RMSNorm */
 
 /* Forward (DeepSpeed PR #8645, Summary and Semantics): float32 statistics

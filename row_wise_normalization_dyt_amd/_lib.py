@@ -31,6 +31,7 @@ SIGNATURES = {
     "layernorm_fwd": (_ci, [_i64, _i64, _vp, _ci, _vp, _vp, _ci, _cf, _vp, _fp, _fp, _vp]),
     "layernorm_bwd": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _fp, _vp, _ci, _cf, _vp, _vp, _vp, _vp, _sz, _vp]),
     "layernorm_bwd_workspace_size": (_ci, [_i64, _i64, _ci, ctypes.POINTER(_sz)]),
+    "layernorm_bwd_noalloc": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _fp, _vp, _ci, _cf, _vp, _vp, _vp, _vp]),
     "rmsnorm_fwd": (_ci, [_i64, _i64, _vp, _ci, _vp, _ci, _cf, _vp, _fp, _vp]),
     "rmsnorm_bwd": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _vp, _ci, _cf, _vp, _vp, _vp, _sz, _vp]),
     "rmsnorm_bwd_workspace_size": (_ci, [_i64, _i64, _ci, ctypes.POINTER(_sz)]),

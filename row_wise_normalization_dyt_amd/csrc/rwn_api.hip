@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/rwnorm.h"
@@ -284,12 +285,42 @@ RWN_API rwn_status layernorm_fwd(int64_t M, int64_t N, const void* x, rwn_dtype 
     return ok();
 }
 
-RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
-                                 rwn_dtype x_dtype, const float* mean, const float* rstd,
-                                 const void* gamma, rwn_dtype param_dtype, float eps, void* dx,
-                                 void* dgamma, void* dbeta, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-    const char* fn = "layernorm_bwd";
+namespace {
+
+// Static scratch of layernorm_bwd_noalloc: the partial rows live in this array instead of a
+// caller workspace.  Each device that runs the library holds its own copy until the process
+// ends; every call on a device shares it.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's copy of `scratch`, looked up once per device (with that
+// device current) and kept.  The array's name is a host-side stand-in in host code: only this
+// address may be handed to kernels.
+rwn_status scratch_address(const char* fn, float** out) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(RWN_ERR_UNSUPPORTED, "%s: device ordinal %d above 63", fn, dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(RWN_ERR_LAUNCH, "%s: hipGetSymbolAddress returned NULL", fn);
+        addr[dev] = p;
+    }
+    *out = (float*)addr[dev];
+    return RWN_OK;
+}
+
+// layernorm_bwd with the partial rows in the caller's workspace, or (static_scratch) in this
+// device's copy of `scratch`.
+rwn_status ln_bwd_impl(const char* fn, int64_t M, int64_t N, const void* x, const void* dy,
+                       rwn_dtype x_dtype, const float* mean, const float* rstd, const void* gamma,
+                       rwn_dtype param_dtype, float eps, void* dx, void* dgamma, void* dbeta,
+                       void* workspace, size_t workspace_bytes, bool static_scratch, void* stream) {
     rwn_status st = check_shape_dtypes(fn, M, N, x_dtype, param_dtype);
     if (st != RWN_OK) return st;
     if ((st = check_eps(fn, eps)) != RWN_OK) return st;
@@ -306,13 +337,43 @@ RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void
     if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
     // No parameter gradient wanted: dx only, no workspace, no stage 2.
     const bool grads = dgamma || dbeta;
-    if (grads && (st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
-    float* ws = grads ? (float*)workspace : nullptr;
+    float* ws = nullptr;
+    if (grads && static_scratch) {
+        const size_t need = (size_t)p.partial_rows() * (size_t)ng * sizeof(float);
+        if (need > kScratchBytes)
+            return fail(RWN_ERR_UNSUPPORTED,
+                        "%s: [%lld, %lld] needs %zu bytes of partial rows, more than the %zu-byte static "
+                        "scratch; call layernorm_bwd with a workspace instead",
+                        fn, (long long)M, (long long)N, need, kScratchBytes);
+        if ((st = scratch_address(fn, &ws)) != RWN_OK) return st;
+    } else if (grads) {
+        if ((st = check_workspace(fn, p, LAYER_LN, workspace, workspace_bytes)) != RWN_OK) return st;
+        ws = (float*)workspace;
+    }
     hipError_t e = traced(RWN_K_LN_BWD, s, [&] {
         return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return finish_bwd(fn, param_dtype, ws, p.partial_rows(), ng, p.ws_rs, p.ws_cs, N, dgamma, dbeta, nullptr, s);
+}
+
+}  // namespace
+
+RWN_API rwn_status layernorm_bwd(int64_t M, int64_t N, const void* x, const void* dy,
+                                 rwn_dtype x_dtype, const float* mean, const float* rstd,
+                                 const void* gamma, rwn_dtype param_dtype, float eps, void* dx,
+                                 void* dgamma, void* dbeta, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return ln_bwd_impl("layernorm_bwd", M, N, x, dy, x_dtype, mean, rstd, gamma, param_dtype, eps, dx,
+                       dgamma, dbeta, workspace, workspace_bytes, false, stream);
+}
+
+RWN_API rwn_status layernorm_bwd_noalloc(int64_t M, int64_t N, const void* x, const void* dy,
+                                         rwn_dtype x_dtype, const float* mean, const float* rstd,
+                                         const void* gamma, rwn_dtype param_dtype, float eps,
+                                         void* dx, void* dgamma, void* dbeta, void* stream) {
+    return ln_bwd_impl("layernorm_bwd_noalloc", M, N, x, dy, x_dtype, mean, rstd, gamma, param_dtype,
+                       eps, dx, dgamma, dbeta, nullptr, 0, true, stream);
 }
 
 RWN_API rwn_status layernorm_bwd_workspace_size(int64_t M, int64_t N, rwn_dtype x_dtype, size_t* bytes) {

@@ -1,0 +1,76 @@
+"""layernorm_bwd_noalloc (partial rows in the library's static device scratch) against
+layernorm_bwd with a caller workspace and against the oracle, called through the C ABI.
+
+Two calls in a row, the second on a smaller input, so the second reuses the scratch the first
+left behind; results must be bitwise those of layernorm_bwd and within the oracle bounds."""
+import ctypes
+
+import pytest
+import torch
+
+import row_wise_normalization_dyt_amd as rwn
+import workloads
+from row_wise_normalization_dyt_amd import _lib
+from tests import gpu_cases as gc
+from tests import tolerance as tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _noalloc(x, dy, mean, rstd, gamma, eps):
+    """One call of layernorm_bwd_noalloc on NaN-filled outputs; returns (dx, dgamma, dbeta)."""
+    lib = _lib.load()
+    M, N = x.shape
+    dx = torch.full_like(x, float("nan"))
+    dg = torch.full((N,), float("nan"), dtype=gamma.dtype, device=x.device)
+    db = torch.full((N,), float("nan"), dtype=gamma.dtype, device=x.device)
+    xdt = {torch.float32: _lib.RWN_F32, torch.bfloat16: _lib.RWN_BF16, torch.float16: _lib.RWN_F16}
+    rc = lib.layernorm_bwd_noalloc(M, N, x.data_ptr(), dy.data_ptr(), xdt[x.dtype], mean.data_ptr(),
+                                   rstd.data_ptr(), gamma.data_ptr(), xdt[gamma.dtype], ctypes.c_float(eps),
+                                   dx.data_ptr(), dg.data_ptr(), db.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    _lib.check(lib, "layernorm_bwd_noalloc", rc)
+    return dx, dg, db
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("shapes", [((401408, 24, "f32", "f32"), (4099, 24, "f32", "f32")),
+                                    ((65536, 1025, "bf16", "f32"), (777, 1025, "bf16", "f32")),
+                                    ((16384, 2048, "bf16", "bf16"), (130, 2048, "bf16", "bf16"))])
+def test_noalloc_matches_workspace_backward_twice(shapes):
+    for (M, N, xdt, pdt) in shapes:
+        wl = workloads.small("layernorm", M, N, xdt, pdt, seed=M % 97 + N)
+        print("case:", wl.name, "noalloc", flush=True)
+        h = workloads.make_inputs(wl)
+        inp = {k: v.to(DEV) for k, v in h.items()}
+        y, mean, rstd = rwn.layernorm_fwd(inp["x"], inp["gamma"], inp["beta"], wl.eps)
+        ref = rwn.layernorm_bwd(inp["x"], inp["dy"], mean, rstd, inp["gamma"], wl.eps)
+        got = _noalloc(inp["x"], inp["dy"], mean, rstd, inp["gamma"], workloads.eps_f32(wl.eps))
+        torch.cuda.synchronize()
+        for a, b, name in zip(got, ref, ("dx", "dgamma", "dbeta")):
+            assert torch.equal(_bits(a), _bits(b)), (wl.name, name)
+        rows = gc.sample_rows(M, k=24)
+        o = gc.oracle_run("layernorm", h, wl.eps, rows=rows)
+        g = {"y": y, "dx": got[0], "dgamma": got[1], "dbeta": got[2]}
+        tol.assert_reports(gc.compare("layernorm", g, o, gc.DT[xdt], gc.DT[pdt], rows=rows))
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch():
+    """A shape whose partial rows exceed the 32 MiB scratch is refused before any launch."""
+    for (M, N) in [(4096, 12288), (4096, 16384), (8192, 8192)]:
+        p = rwn.plan("layernorm", True, M, N, torch.float32)
+        if p["grid"] * 2 * N * 4 > 32 << 20:
+            break
+    else:
+        pytest.skip("no candidate shape plans more than 32 MiB of partial rows on this device")
+    print("case: noalloc rejection", M, N, p["grid"], flush=True)
+    x = torch.zeros(M, N, device=DEV)
+    g = torch.ones(N, device=DEV)
+    st = torch.zeros(M, device=DEV)
+    with pytest.raises(rwn.RwnError, match="static"):
+        _noalloc(x, x, st, st, g, 1e-5)
