@@ -196,9 +196,14 @@ typedef enum {
 rwn_status rwn_trace_begin(int capacity);
 int rwn_trace_end(float* ms, int* tags, int capacity);
 
-/* Bandwidth probe, a measurement aid: copies `bytes` from src to dst with 16-byte vector
- * loads and stores (both 16-byte aligned, bytes a multiple of 16), enqueued on `stream`. */
-rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream);
+/* Streaming probe, a measurement aid: dst = src (src2 NULL) or dst = src XOR src2 over `bytes`
+ * (all buffers 16-byte aligned, bytes a multiple of 16), enqueued on `stream`.  A persistent
+ * grid of wg_per_cu (1..32) 256-thread workgroups per CU; every lane keeps `unroll` (1, 2, 4 or 8)
+ * 16-byte loads per input in flight before it stores; nontemporal != 0 puts the streaming hint
+ * on every access.  It bounds the rate of a kernel that reads one or two tensors of that size
+ * and writes one. */
+rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t bytes, int unroll,
+                            int nontemporal, int wg_per_cu, void* stream);
 
 /* Launch plan the library chooses for an entry point (introspection for tests and tuning).
  * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 15 integers to out:

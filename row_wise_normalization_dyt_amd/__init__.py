@@ -16,7 +16,7 @@ import torch
 from . import _lib
 
 __all__ = ["dyt_fwd", "dyt_bwd", "layernorm_fwd", "layernorm_bwd", "rmsnorm_fwd", "rmsnorm_bwd",
-           "workspace_size", "version", "trace_begin", "trace_end", "copy_probe", "plan", "RwnError"]
+           "workspace_size", "version", "trace_begin", "trace_end", "stream_probe", "plan", "RwnError"]
 
 RwnError = _lib.RwnError
 _DT = {torch.float32: _lib.RWN_F32, torch.bfloat16: _lib.RWN_BF16, torch.float16: _lib.RWN_F16}
@@ -316,14 +316,19 @@ def trace_end(capacity: int = 4096):
     return [(_lib.KERNEL_TAGS.get(tags[i], str(tags[i])), float(ms[i])) for i in range(n)]
 
 
-def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
-    """dst[:] = src[:] with the library's 16-byte-vector copy kernel (a bandwidth probe)."""
+def stream_probe(src: torch.Tensor, dst: torch.Tensor, src2: Optional[torch.Tensor] = None, unroll: int = 4,
+                 nontemporal: bool = True, wg_per_cu: int = 8) -> None:
+    """dst[:] = src (or src XOR src2) with the library's streaming probe kernel (a bandwidth
+    measurement aid; every tensor's bytes are copied as opaque 16-byte chunks)."""
     lib = _L()
-    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
-        raise ValueError("copy_probe: sizes differ")
+    n = src.numel() * src.element_size()
+    for t in (dst, src2):
+        if t is not None and t.numel() * t.element_size() != n:
+            raise ValueError("stream_probe: sizes differ")
     with torch.cuda.device(src.device):
-        _lib.check(lib, "rwn_copy_probe", lib.rwn_copy_probe(src.data_ptr(), dst.data_ptr(),
-                                                             src.numel() * src.element_size(), _stream(src.device)))
+        _lib.check(lib, "rwn_stream_probe", lib.rwn_stream_probe(src.data_ptr(), _ptr(src2), dst.data_ptr(), n,
+                                                                 int(unroll), int(bool(nontemporal)), int(wg_per_cu),
+                                                                 _stream(src.device)))
 
 
 def plan(layer: str, backward: bool, M: int, N: int, dtype: torch.dtype, misalign_bytes: int = 0,

@@ -19,7 +19,7 @@ RWN_F32, RWN_BF16, RWN_F16 = 0, 1, 2
 STATUS = {0: "RWN_OK", 1: "RWN_ERR_INVALID_ARG", 2: "RWN_ERR_UNSUPPORTED", 3: "RWN_ERR_WORKSPACE",
           4: "RWN_ERR_LAUNCH"}
 KERNEL_TAGS = {1: "dyt_fwd", 2: "dyt_bwd", 3: "layernorm_fwd", 4: "layernorm_bwd", 5: "rmsnorm_fwd",
-               6: "rmsnorm_bwd", 7: "colreduce", 8: "copy_probe"}
+               6: "rmsnorm_bwd", 7: "colreduce", 8: "stream_probe"}
 
 _i64, _vp, _ci, _cf, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _fp = ctypes.c_void_p   # float* (device)
@@ -41,7 +41,7 @@ SIGNATURES = {
     "rwn_version": (ctypes.c_char_p, []),
     "rwn_trace_begin": (_ci, [_ci]),
     "rwn_trace_end": (_ci, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int), _ci]),
-    "rwn_copy_probe": (_ci, [_vp, _vp, _sz, _vp]),
+    "rwn_stream_probe": (_ci, [_vp, _vp, _vp, _sz, _ci, _ci, _ci, _vp]),
     "rwn_plan": (_ci, [_ci, _ci, _i64, _i64, _ci, _ci, _ci, _ci, ctypes.POINTER(_i64)]),
 }
 

@@ -368,21 +368,65 @@ hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int
     }
 }
 
-// Bandwidth probe: 16-byte vector copy, grid-stride.
+// Streaming probe (a measurement aid): out = a (one input) or out = a ^ b (two inputs) over n16
+// 16-byte chunks.  A persistent grid of wg_per_cu workgroups per CU; each lane keeps U 16-byte
+// loads per input in flight (chunks i, i + S, ..., i + (U - 1) S, S the grid's thread count)
+// before it stores, optionally with the nontemporal hint on every access.  It bounds what a
+// kernel that reads one or two tensors and writes one can stream at a given size.
+template <int U, bool TWO, bool NT>
 __global__ void __launch_bounds__(256)
-copy_probe_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst, int64_t n16) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-         i += (int64_t)gridDim.x * blockDim.x)
-        dst[i] = src[i];
+stream_probe_kernel(const u32x4* __restrict__ a, const u32x4* __restrict__ b, u32x4* __restrict__ o,
+                    int64_t n16) {
+    const int64_t S = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    auto ld = [](const u32x4* p) { return NT ? __builtin_nontemporal_load(p) : *p; };
+    for (; i + (U - 1) * S < n16; i += U * S) {
+        u32x4 v[U], w[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = ld(a + i + j * S);
+        if constexpr (TWO) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) w[j] = ld(b + i + j * S);
+#pragma unroll
+            for (int j = 0; j < U; ++j) v[j] ^= w[j];
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if constexpr (NT) __builtin_nontemporal_store(v[j], o + i + j * S);
+            else o[i + j * S] = v[j];
+        }
+    }
+    for (; i < n16; i += S) {
+        u32x4 v = ld(a + i);
+        if constexpr (TWO) v ^= ld(b + i);
+        if constexpr (NT) __builtin_nontemporal_store(v, o + i);
+        else o[i] = v;
+    }
 }
 
-hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s) {
+hipError_t launch_stream_probe(const void* a, const void* b, void* out, size_t bytes, int unroll,
+                               int nontemporal, int wg_per_cu, int cus, hipStream_t s) {
     const int64_t n16 = (int64_t)(bytes / 16);
-    int64_t grid = (n16 + 255) / 256;
-    if (grid > 65536) grid = 65536;
+    int64_t grid = (int64_t)cus * wg_per_cu;
+    const int64_t need = (n16 + 255) / 256;
+    if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    return launch(copy_probe_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const f32x4*)src,
-                  (f32x4*)dst, n16);
+    const dim3 g((unsigned)grid), blk(256);
+    const u32x4 *pa = (const u32x4*)a, *pb = (const u32x4*)b;
+    u32x4* po = (u32x4*)out;
+    auto go = [&](auto u, auto two, auto nt) {
+        return launch(stream_probe_kernel<decltype(u)::value, decltype(two)::value != 0, decltype(nt)::value != 0>, g,
+                      blk, 0, s, pa, pb, po, n16);
+    };
+    auto by_nt = [&](auto u, auto two) { return nontemporal ? go(u, two, IC<1>{}) : go(u, two, IC<0>{}); };
+    auto by_two = [&](auto u) { return b ? by_nt(u, IC<1>{}) : by_nt(u, IC<0>{}); };
+    switch (unroll) {
+    case 1: return by_two(IC<1>{});
+    case 2: return by_two(IC<2>{});
+    case 4: return by_two(IC<4>{});
+    case 8: return by_two(IC<8>{});
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace rwn

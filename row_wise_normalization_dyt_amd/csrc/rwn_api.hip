@@ -545,14 +545,24 @@ RWN_API int rwn_trace_end(float* ms, int* tags, int capacity) {
     return n;
 }
 
-RWN_API rwn_status rwn_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
-    if (!src || !dst) return fail(RWN_ERR_INVALID_ARG, "rwn_copy_probe: NULL buffer");
-    if (((uintptr_t)src | (uintptr_t)dst | bytes) % 16)
-        return fail(RWN_ERR_INVALID_ARG, "rwn_copy_probe: buffers and size must be 16-byte multiples");
+RWN_API rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t bytes, int unroll,
+                                    int nontemporal, int wg_per_cu, void* stream) {
+    const char* fn = "rwn_stream_probe";
+    if (!src || !dst) return fail(RWN_ERR_INVALID_ARG, "%s: NULL buffer", fn);
+    if (((uintptr_t)src | (uintptr_t)src2 | (uintptr_t)dst | bytes) % 16)
+        return fail(RWN_ERR_INVALID_ARG, "%s: buffers and size must be 16-byte multiples", fn);
+    if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+        return fail(RWN_ERR_INVALID_ARG, "%s: unroll must be 1, 2, 4 or 8", fn);
+    if (wg_per_cu < 1 || wg_per_cu > 32) return fail(RWN_ERR_INVALID_ARG, "%s: wg_per_cu must be in [1, 32]", fn);
     if (bytes == 0) return ok();
+    int cus = 0;
+    rwn_status st = device_cus(&cus);
+    if (st != RWN_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = traced(RWN_K_COPY, s, [&] { return launch_copy_probe(src, dst, bytes, s); });
-    if (e != hipSuccess) return hip_fail(e, "rwn_copy_probe");
+    hipError_t e = traced(RWN_K_COPY, s, [&] {
+        return launch_stream_probe(src, src2, dst, bytes, unroll, nontemporal != 0, wg_per_cu, cus, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 

@@ -207,6 +207,7 @@ hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const vo
 // out0 [N], out1 [N], out2 [1] in param dtype pdt.
 hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
                             int64_t N, void* out0, void* out1, void* out2, hipStream_t s);
-hipError_t launch_copy_probe(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_stream_probe(const void* a, const void* b, void* out, size_t bytes, int unroll,
+                               int nontemporal, int wg_per_cu, int cus, hipStream_t s);
 
 }  // namespace rwn

@@ -105,8 +105,10 @@ def test_workspace_query_errors(lib):
 def test_trace_and_probe_argument_errors(lib):
     assert lib.rwn_trace_begin(0) == 1
     assert lib.rwn_trace_end(None, None, 0) == -1
-    assert lib.rwn_copy_probe(None, P, 16, None) == 1
-    assert lib.rwn_copy_probe(P, P, 24, None) == 1
+    assert lib.rwn_stream_probe(None, None, P, 16, 4, 1, 8, None) == 1
+    assert lib.rwn_stream_probe(P, None, P, 24, 4, 1, 8, None) == 1
+    assert lib.rwn_stream_probe(P, None, P, 32, 3, 1, 8, None) == 1
+    assert lib.rwn_stream_probe(P, None, P, 32, 4, 1, 0, None) == 1
 
 
 # ------------------------------------------------------------------------------ planning

@@ -62,14 +62,15 @@ def test_noalloc_matches_workspace_backward_twice(shapes):
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     """A shape whose partial rows exceed the 32 MiB scratch is refused before any launch."""
-    for (M, N) in [(4096, 12288), (4096, 16384), (8192, 8192)]:
-        p = rwn.plan("layernorm", True, M, N, torch.float32)
+    for (M, N, dt) in [(4096, 12288, torch.bfloat16), (4096, 10240, torch.bfloat16), (4096, 12288, torch.float32),
+                       (4096, 16384, torch.float32), (8192, 8192, torch.float32)]:
+        p = rwn.plan("layernorm", True, M, N, dt)
         if p["grid"] * 2 * N * 4 > 32 << 20:
             break
     else:
         pytest.skip("no candidate shape plans more than 32 MiB of partial rows on this device")
-    print("case: noalloc rejection", M, N, p["grid"], flush=True)
-    x = torch.zeros(M, N, device=DEV)
+    print("case: noalloc rejection", M, N, dt, p["grid"], flush=True)
+    x = torch.zeros(M, N, device=DEV, dtype=dt)
     g = torch.ones(N, device=DEV)
     st = torch.zeros(M, device=DEV)
     with pytest.raises(rwn.RwnError, match="static"):

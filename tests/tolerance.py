@@ -43,13 +43,15 @@ class Report:
     max_ulp: float          # max error in output-dtype ulps
     within_1ulp: float      # fraction of elements within one ulp
     worst: Optional[tuple]
+    outside_policy: int = 0  # elements outside |gpu - exact| <= 2^-6 + 2^-6 |exact| (the BF16 policy)
 
     def ok(self) -> bool:
         return self.bad == 0
 
     def __str__(self):
         return (f"{self.name}: n={self.n} bad={self.bad} max_err/bound={self.max_ratio:.3g} "
-                f"max_ulp={self.max_ulp:.3g} within_1ulp={self.within_1ulp:.5f} worst={self.worst}")
+                f"max_ulp={self.max_ulp:.3g} within_1ulp={self.within_1ulp:.5f} "
+                f"outside_bf16_policy={self.outside_policy} worst={self.worst}")
 
 
 def compare(name: str, gpu: torch.Tensor, exact: np.ndarray, scale: np.ndarray, out_dtype: torch.dtype,
@@ -77,11 +79,11 @@ def compare(name: str, gpu: torch.Tensor, exact: np.ndarray, scale: np.ndarray, 
         k = int(np.nanargmax(np.where(np.isfinite(ratio), ratio, 1e300)))
         idx = np.unravel_index(k, err.shape)
         worst = (tuple(int(i) for i in idx), float(g.reshape(err.shape)[idx]), float(ex[idx]), float(bound[idx]))
-    finite_ratio = ratio[np.isfinite(ratio)]
+    policy_bad = int((~((err <= 2.0 ** -6 + 2.0 ** -6 * np.abs(ex)) | both_nan | same_inf)).sum())
     return Report(name, int(err.size), bad,
                   float(np.max(ratio)) if ratio.size else 0.0,
                   float(np.nanmax(ulps)) if ulps.size else 0.0,
-                  float(np.mean(ulps <= 1.0)) if ulps.size else 1.0, worst)
+                  float(np.mean(ulps <= 1.0)) if ulps.size else 1.0, worst, policy_bad)
 
 
 def compare_param(name: str, gpu: torch.Tensor, exact: np.ndarray, abs_sum: np.ndarray,
@@ -104,7 +106,8 @@ def compare_param(name: str, gpu: torch.Tensor, exact: np.ndarray, abs_sum: np.n
         worst = (k, float(g[k]), float(ex[k]), float(bound[k]))
     return Report(name, int(err.size), bad, float(np.max(ratio)) if ratio.size else 0.0,
                   float(np.max(err / u)) if err.size else 0.0,
-                  float(np.mean(err <= u)) if err.size else 1.0, worst)
+                  float(np.mean(err <= u)) if err.size else 1.0, worst,
+                  int((err > 2.0 ** -6 + 2.0 ** -6 * np.abs(ex)).sum()))
 
 
 def merge(reports) -> Report:
@@ -114,7 +117,8 @@ def merge(reports) -> Report:
     worst = max(reports, key=lambda r: r.max_ratio)
     return Report(reports[0].name, n, sum(r.bad for r in reports), max(r.max_ratio for r in reports),
                   max(r.max_ulp for r in reports),
-                  sum(r.within_1ulp * r.n for r in reports) / n if n else 1.0, worst.worst)
+                  sum(r.within_1ulp * r.n for r in reports) / n if n else 1.0, worst.worst,
+                  sum(r.outside_policy for r in reports))
 
 
 def assert_reports(reports) -> None:
