@@ -40,11 +40,13 @@
  *            may be NULL.
  * Gradients  First-order only; eps is a constant.
  * Width      1 <= N <= 16384.  A row is cut into 16-byte chunks (4 float32 / 8 bfloat16 or
- *            float16 elements) spread over at most 1024 threads; when N is not a multiple of the chunk
- *            or the operands are not 16-byte aligned a row may straddle one more chunk, so
- *            those LayerNorm/RMSNorm calls take N <= 16381 (float32) / 16377 (16-bit) and
- *            otherwise return RWN_ERR_UNSUPPORTED.  DyT splits wide rows into column blocks
- *            and takes every N up to 16384.
+ *            float16 elements) spread over at most 1024 threads.  A wide row that is not a whole
+ *            number of aligned chunks (N not a multiple of the chunk, or operands not 16-byte
+ *            aligned) is cut into its aligned chunks plus up to 2 * chunk - 2 single head and
+ *            tail elements; float32 LayerNorm/RMSNorm rows of that kind wider than 8192 instead
+ *            straddle one more chunk, so those calls take N <= 16381 and otherwise return
+ *            RWN_ERR_UNSUPPORTED.  DyT splits wide rows into column blocks and takes every N up
+ *            to 16384.
  */
 #ifndef RWNORM_H
 #define RWNORM_H
@@ -206,7 +208,7 @@ rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t
                             int nontemporal, int wg_per_cu, void* stream);
 
 /* Launch plan the library chooses for an entry point (introspection for tests and tuning).
- * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 15 integers to out:
+ * layer: 0 = DyT, 1 = LayerNorm, 2 = RMSNorm; backward: 0/1.  Writes 16 integers to out:
  * {mode (0 aligned vectors, 1 shifted vectors, 2 scalar), chunks per thread, rows per thread,
  *  threads per row, row slots per workgroup, workgroup size, workgroups, row tiles,
  *  elements per chunk, row tiles per workgroup (0 when strided), strided (1: workgroup w
@@ -214,7 +216,8 @@ rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t
  *  (1: workgroup numbers renumbered so consecutive ones share an XCD), prefetch (1: the next
  *  tile's loads are issued before the current tile is processed), flat (1: narrow aligned
  *  LayerNorm rows through plain loads on clamped row indices instead of per-tile buffer
- *  descriptors)}.  param_dtype: the parameter
+ *  descriptors), split (1: a wide row not aligned to 16-byte chunks is cut into whole aligned
+ *  chunks plus scalar head and tail elements)}.  param_dtype: the parameter
  * dtype of a forward (-1: any; a backward is always planned for every parameter dtype, as its
  * workspace is).  misalign_bytes is the common address of x/y/dy/dx modulo 16.  cus: 0 plans
  * for the current device exactly as the entry points do (its CU count, and the workgroups of

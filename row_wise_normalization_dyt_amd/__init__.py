@@ -336,10 +336,10 @@ def plan(layer: str, backward: bool, M: int, N: int, dtype: torch.dtype, misalig
     """The launch plan the library picks.  cus = 0 plans for the current device, as the entry
     points do; any other value plans for that many compute units without touching a device."""
     lib = _L()
-    out = (ctypes.c_int64 * 15)()
+    out = (ctypes.c_int64 * 16)()
     li = {"dyt": 0, "layernorm": 1, "rmsnorm": 2}[layer]
     pd = -1 if param_dtype is None else _DT[param_dtype]
     _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], pd, misalign_bytes, cus, out))
     keys = ("mode", "cpt", "rt", "tpr", "rpp", "block", "grid", "ntiles", "vec", "kt", "strided", "ncb", "xcd_remap",
-            "prefetch", "flat")
+            "prefetch", "flat", "split")
     return dict(zip(keys, [int(v) for v in out]))

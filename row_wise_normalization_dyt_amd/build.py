@@ -12,8 +12,8 @@ BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "librwnorm.so")
 
 SOURCES = ["rwn_api.hip", "launch_common.hip", "launch_dyt.hip", "launch_layernorm.hip",
-           "launch_flat.hip", "launch_rmsnorm.hip"]
-HEADERS = ["rwn_device.hpp", "rwn_kernels.hpp", "rwn_launch.hpp"]
+           "launch_flat.hip", "launch_rmsnorm.hip", "launch_split.hip"]
+HEADERS = ["rwn_device.hpp", "rwn_kernels.hpp", "rwn_launch.hpp", "rwn_split.hpp"]
 
 ARCH = os.environ.get("RWN_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,6 +8,7 @@
 
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
+#include "rwn_split.hpp"
 
 namespace rwn {
 
@@ -39,6 +40,10 @@ static int64_t next_pow2(int64_t v) {
 //                           they exist (and with it the general LayerNorm kernels)
 //   RWN_FLAT                0: narrow aligned LayerNorm rows take the general kernels (default 1:
 //                           the flat kernels)
+//   RWN_SPLIT               0: wide rows take the general kernels only (default 1: the split-row
+//                           kernels for unaligned wide rows and the aligned ones they measured
+//                           faster on; 2: for every wide row)
+//   RWN_SPLIT_CPT           1, 2 or 4: chunks per lane of split-row plans
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -67,6 +72,130 @@ int kernel_occupancy(const void* kernel, int block, size_t dyn_lds) {
     return n;
 }
 
+static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pdt);
+
+// Persistent grid-stride with c workgroups per CU, all resident at once (occ: workgroups of the
+// kernel that fit on a CU, 0 if unknown).  c spans [16, 28] resident waves per CU (fewer waves
+// leave HBM latency exposed; more add nothing).  Within that range the c whose tile count per
+// workgroup is most even wins: the kernel lasts as long as its busiest workgroup, so ntiles / gt
+// against ceil(ntiles / gt) is the fraction of the machine kept busy to the end.  Each extra
+// workgroup per CU must buy 2% of balance (measured: narrow LayerNorm backwards at 28 waves per
+// CU run 20% slower than at 20).  With ncb column blocks the grid is ncb workgroups per tile
+// stride.  The tile stride is a multiple of 8, so rows it separates start at the same offset
+// modulo 16 bytes.
+static void persistent_grid(Plan& p, int cus, int64_t occ, int wg_per_cu, int min_waves) {
+    const int64_t waves_per_wg = (p.block + 63) / 64;
+    int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
+    if (occ > 0) c_max = std::min(c_max, occ);
+    const int64_t c_lo = std::min(c_max, std::max<int64_t>(1, (min_waves + waves_per_wg - 1) / waves_per_wg));
+    const int64_t c_hi = std::max<int64_t>(c_lo, std::min<int64_t>(c_max, 28 / waves_per_wg));
+    int64_t gt = 0;
+    double best = -1.0;
+    for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
+        if (wg_per_cu > 0 && cc != wg_per_cu) continue;
+        int64_t cand = (int64_t)cus * cc / p.ncb;
+        cand -= cand % 8;                  // SHIFTED: the tile stride * rpp must be a multiple of V
+        if (cand < 8) cand = 8;
+        if (cand >= p.ntiles) { gt = p.ntiles; break; }   // one tile per workgroup
+        const double per = (double)p.ntiles / (double)cand;
+        const double eff = per / std::ceil(per) - 0.02 * (double)(cc - c_lo);
+        if (eff > best + 1e-9) { best = eff; gt = cand; }
+    }
+    if (gt == 0) {   // forced c out of range: nearest in-range candidate
+        gt = (int64_t)cus * (wg_per_cu > 0 ? std::min<int64_t>(wg_per_cu, c_max) : c_lo) / p.ncb;
+        gt -= gt % 8;
+        if (gt < 8) gt = 8;
+        if (gt > p.ntiles) gt = p.ntiles;
+    }
+    p.grid = gt * p.ncb;
+}
+
+// Backward partials: column-major when rows are short (stage 2 then reads each column
+// contiguously), row-major when wide (stage 1 then writes each row contiguously).
+static void partial_layout(int layer, Plan& p) {
+    const int64_t ng = partial_cols(layer, p.N, p.ncb);
+    if (ng <= 1024) {
+        p.ws_rs = 1;
+        p.ws_cs = p.partial_rows();
+    } else {
+        p.ws_rs = ng;
+        p.ws_cs = 1;
+    }
+}
+
+// Split-row plan (rwn_split.hpp) for a wide row: W <= max_w waves per row
+// slot and CPT whole chunks per lane covering the row's aligned middle, head and tail elements as
+// scalar slots (measured at 65536 x 1025 bf16, against one chunk per lane: DyT forward 73.0 ->
+// 59.9 us, RMSNorm backward 87.3 -> 83.3 us; four per lane spill in backwards).  Slots fill
+// 512-thread workgroups; a backward combines its
+// slots' partials in LDS (NG gradients x N floats) when that fits in 48 KB, else takes one slot
+// per workgroup.  Returns false where no shape fits (float32 rows wider than 8192), leaving the
+// general kernels' shifted mode.
+static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int b, int cus,
+                       bool occupancy, int wg_per_cu, int min_waves, int xcd_remap, int max_w, Plan* pp) {
+    static const int split_cpt = env_int("RWN_SPLIT_CPT", 1, 4, 0);
+    Plan& p = *pp;
+    const int esz = xdt == DT_F32 ? 4 : 2;
+    const int V = 16 / esz;
+    const int64_t nm = N / V;   // most whole chunks a row can hold (a row starting aligned)
+    // Chunks per lane: 16 elements per lane (2 bfloat16 / float16 chunks, 4 float32 ones), or
+    // half that where it takes fewer lane slots; 32 elements only for LayerNorm / RMSNorm rows
+    // too wide for 8 waves otherwise (DyT's backward would spill: its wide rows keep the general
+    // kernels' column blocks).
+    const int pref = 16 / V;
+    const bool wide_ok = layer != LAYER_DYT && max_w >= 8;   // rows no other plan takes
+    int bw = 0, bc = 0;
+    int64_t best_slots = -1;
+    const int cands[3] = {pref, pref / 2, pref * 2};
+    for (int ci = 0; ci < 3; ++ci) {
+        const int c = cands[ci];
+        if (c < 1 || c > 4 || (ci == 2 && !wide_ok)) continue;
+        if (split_cpt > 0 && c != split_cpt) continue;
+        const int64_t w = (nm + 64 * c - 1) / (64 * c);
+        if (w > max_w) continue;
+        const int64_t slots = 64 * w * c;
+        if (ci == 2 && bw) continue;   // only when nothing narrower fits
+        if (best_slots < 0 || slots < best_slots) {
+            best_slots = slots;
+            bw = (int)w;
+            bc = c;
+        }
+    }
+    if (bw == 0) return false;
+    p.mode = MODE_SHIFTED;
+    p.split = 1;
+    p.base_shift = b;
+    p.cpt = bc;
+    p.rt = 1;
+    p.tpr = 64 * bw;
+    p.rpp = std::max(1, kSplitBlock / p.tpr);
+    p.ncb = 1;
+    p.pf = 0;
+    p.flat = 0;
+    const int ngrad = layer == LAYER_RMS ? 1 : 2;
+    if (backward && p.rpp > 1 && (int64_t)ngrad * N * 4 > 48 * 1024) p.rpp = 1;
+    p.block = p.tpr * p.rpp;
+    p.lds_bytes = (backward && p.rpp > 1) ? (size_t)ngrad * N * sizeof(float) : 0;
+    p.ntiles = (M + p.rpp - 1) / p.rpp;
+    int64_t occ = 0;
+    if (occupancy) {
+        const int pdts[3] = {DT_F32, DT_BF16, DT_F16};
+        for (int i = 0; i < 3; ++i) {
+            if (pdt >= 0 && pdts[i] != pdt) continue;
+            if (!dtype_pair_ok(xdt, pdts[i])) continue;
+            const int n = resident_wgs(layer, backward, p, xdt, pdts[i]);
+            if (n > 0) occ = occ == 0 ? n : std::min<int64_t>(occ, n);
+        }
+    }
+    p.strided = 1;
+    p.kt = 0;
+    persistent_grid(p, cus, occ, wg_per_cu, min_waves);
+    const bool remap = xcd_remap >= 0 ? xcd_remap == 1 : true;
+    p.xcd_remap = (remap && p.grid % 8 == 0) ? 1 : 0;
+    if (backward) partial_layout(layer, p);
+    return true;
+}
+
 static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pdt) {
     if (layer == LAYER_DYT) return resident_wgs_dyt(backward, p, xdt, pdt);
     if (layer == LAYER_LN) return resident_wgs_ln(backward, p, xdt, pdt);
@@ -86,6 +215,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int wide_cpt = env_int("RWN_WIDE_CPT", 1, 4, 0);
     static const int packed_rows = env_int("RWN_PACKED_ROWS", 0, 1, 1);
     static const int flat_rows = env_int("RWN_FLAT", 0, 1, 1);
+    static const int split_rows = env_int("RWN_SPLIT", 0, 2, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -107,6 +237,23 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             p.mode = MODE_SCALAR;
             chunks = N;
         }
+    }
+    // Split-row kernels: every wide row not aligned to 16-byte chunks, and aligned wide rows of at
+    // most max_w waves per row slot.  Measured against the general kernels (65536 x N bf16, forward
+    // / backward us): N = 1024 LayerNorm 58.1 / 88.5 -> 48.6 / 86.4, RMSNorm 50.7 / 78.5 -> 46.6 /
+    // 73.8, DyT 60.8 / 82.9 -> 50.1 / 81.6; N = 4096 forwards 182.2 -> 174.4 (LayerNorm), 206.5 ->
+    // 191.1 (DyT), DyT backward 315.2 -> 306.8; 16384 x 2048 RMSNorm 27.2 / 45.8 -> 25.4 / 44.6.
+    // LayerNorm / RMSNorm backwards of four or more waves per row ran slower split (65536 x 4096:
+    // 288.2 -> 332.0, 271.5 -> 284.3 us), and forwards of eight no faster (N = 8192).
+    int split_max_w = 0;
+    if (p.mode == MODE_SHIFTED) split_max_w = 8;
+    else if (p.mode == MODE_ALIGNED && chunks > 64)
+        split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT) ? 4 : 2;
+    if (split_max_w && split_rows && prefetch < 0 &&
+        plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, xcd_remap,
+                   split_max_w, &p)) {
+        *out = p;
+        return true;
     }
     const int v_elems = p.mode == MODE_SCALAR ? 1 : V;
     bool packed = false;   // DyT SHIFTED rows packed into workgroups without wave alignment
@@ -273,39 +420,8 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.kt = blocked_k;
         p.grid = (p.ntiles + p.kt - 1) / p.kt;
     } else {
-        // Persistent grid-stride with c workgroups per CU, all resident at once.  c spans
-        // [16, 28] resident waves per CU (fewer waves leave HBM latency exposed; more add
-        // nothing).  Within that range the c whose tile count per workgroup is most even wins:
-        // the kernel lasts as long as its busiest workgroup, so ntiles / gt against
-        // ceil(ntiles / gt) is the fraction of the machine kept busy to the end.  Each extra
-        // workgroup per CU must buy 2% of balance (measured: narrow LayerNorm backwards at 28
-        // waves per CU run 20% slower than at 20).  With ncb column blocks the grid is ncb
-        // workgroups per tile stride.
         p.strided = 1;
-        const int64_t waves_per_wg = (p.block + 63) / 64;
-        int64_t c_max = std::max<int64_t>(1, 32 / waves_per_wg);   // 32 waves per CU at most
-        if (occ > 0) c_max = std::min(c_max, occ);
-        const int64_t c_lo = std::min(c_max, std::max<int64_t>(1, (min_waves + waves_per_wg - 1) / waves_per_wg));
-        const int64_t c_hi = std::max<int64_t>(c_lo, std::min<int64_t>(c_max, 28 / waves_per_wg));
-        int64_t gt = 0;
-        double best = -1.0;
-        for (int64_t cc = c_lo; cc <= c_hi; ++cc) {
-            if (wg_per_cu > 0 && cc != wg_per_cu) continue;
-            int64_t cand = (int64_t)cus * cc / p.ncb;
-            cand -= cand % 8;                  // SHIFTED: the tile stride * rpp must be a multiple of V
-            if (cand < 8) cand = 8;
-            if (cand >= p.ntiles) { gt = p.ntiles; break; }   // one tile per workgroup
-            const double per = (double)p.ntiles / (double)cand;
-            const double eff = per / std::ceil(per) - 0.02 * (double)(cc - c_lo);
-            if (eff > best + 1e-9) { best = eff; gt = cand; }
-        }
-        if (gt == 0) {   // forced c out of range: nearest in-range candidate
-            gt = (int64_t)cus * (wg_per_cu > 0 ? std::min<int64_t>(wg_per_cu, c_max) : c_lo) / p.ncb;
-            gt -= gt % 8;
-            if (gt < 8) gt = 8;
-            if (gt > p.ntiles) gt = p.ntiles;
-        }
-        p.grid = gt * p.ncb;
+        persistent_grid(p, cus, occ, wg_per_cu, min_waves);
         p.kt = 0;
         // XCD-contiguous numbering pays where a row spans a wave or more (LayerNorm / RMSNorm
         // 65536 x 4096..8192 bf16: 4-6% faster): neighbouring rows share cache lines at their
@@ -316,18 +432,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         const bool remap = xcd_remap >= 0 ? xcd_remap == 1 : p.tpr >= 64;
         p.xcd_remap = (remap && p.grid % 8 == 0) ? 1 : 0;
     }
-    if (backward) {
-        // Partials column-major when rows are short (stage 2 then reads each column
-        // contiguously), row-major when wide (stage 1 then writes each row contiguously).
-        const int64_t ng = partial_cols(layer, N, p.ncb);
-        if (ng <= 1024) {
-            p.ws_rs = 1;
-            p.ws_cs = p.partial_rows();
-        } else {
-            p.ws_rs = ng;
-            p.ws_cs = 1;
-        }
-    }
+    if (backward) partial_layout(layer, p);
     *out = p;
     return true;
 }

@@ -8,6 +8,7 @@ namespace rwn {
 
 hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
                           const void* gamma, const void* beta, void* y, hipStream_t s) {
+    if (p.split) return launch_dyt_fwd_split(p, xdt, pdt, x, alpha, gamma, beta, y, s);
     const Geom g = make_geom(p);
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
@@ -27,6 +28,7 @@ hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
 hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                           const void* alpha, const void* gamma, void* dx, float* ws,
                           hipStream_t s) {
+    if (p.split) return launch_dyt_bwd_split(p, xdt, pdt, x, dy, alpha, gamma, dx, ws, s);
     const Geom g = make_geom(p);
     return dispatch_pg(ws, [&](auto pg) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
@@ -46,6 +48,7 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
 }
 
 int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt) {
+    if (p.split) return resident_wgs_split(LAYER_DYT, backward, p, xdt, pdt);
     int n = 0;
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;

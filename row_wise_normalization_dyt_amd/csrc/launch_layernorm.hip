@@ -8,6 +8,7 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
                          const void* beta, float eps, void* y, float* mean, float* rstd,
                          hipStream_t s) {
     const Geom g = make_geom(p);
+    if (p.split) return launch_ln_fwd_split(p, xdt, pdt, x, gamma, beta, eps, y, mean, rstd, s);
     if (p.flat) return launch_ln_fwd_flat(p, xdt, pdt, x, gamma, beta, eps, y, mean, rstd, s);
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
@@ -27,6 +28,7 @@ hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const v
                          const float* mean, const float* rstd, const void* gamma, float eps,
                          void* dx, float* ws, hipStream_t s) {
     const Geom g = make_geom(p);
+    if (p.split) return launch_ln_bwd_split(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, s);
     if (p.flat) return launch_ln_bwd_flat(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, s);
     return dispatch_pg(ws, [&](auto pg) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
@@ -46,6 +48,7 @@ hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const v
 
 int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt) {
     int n = 0;
+    if (p.split) return resident_wgs_split(LAYER_LN, backward, p, xdt, pdt);
     if (p.flat) return resident_wgs_ln_flat(backward, p, xdt, pdt);
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;

@@ -17,6 +17,7 @@ hipError_t dispatch_variant(int variant, Geom& g, F&& f) {
 
 hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                           float eps, void* y, float* rstd, hipStream_t s) {
+    if (p.split) return launch_rms_fwd_split(p, xdt, pdt, variant, x, w, eps, y, rstd, s);
     Geom g = make_geom(p);
     return dispatch_variant(variant, g, [&](auto var) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
@@ -37,6 +38,7 @@ hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const vo
 hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
                           const float* rstd, const void* w, float eps, void* dx, float* ws,
                           hipStream_t s) {
+    if (p.split) return launch_rms_bwd_split(p, xdt, pdt, variant, x, dy, rstd, w, eps, dx, ws, s);
     Geom g = make_geom(p);
     return dispatch_variant(variant, g, [&](auto var) {
         return dispatch_pg(ws, [&](auto pg) {
@@ -58,6 +60,7 @@ hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const vo
 }
 
 int resident_wgs_rms(bool backward, const Plan& p, int xdt, int pdt) {
+    if (p.split) return resident_wgs_split(LAYER_RMS, backward, p, xdt, pdt);
     int n = 0;
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;

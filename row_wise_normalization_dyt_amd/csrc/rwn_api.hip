@@ -598,5 +598,6 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
     out[12] = p.xcd_remap;
     out[13] = p.pf;
     out[14] = p.flat;
+    out[15] = p.split;
     return ok();
 }

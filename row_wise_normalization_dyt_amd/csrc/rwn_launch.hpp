@@ -38,6 +38,7 @@ struct Plan {
     int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
     int xcd_remap = 0;        // renumber workgroups XCD-contiguously (needs grid % 8 == 0)
     int flat = 0;             // LayerNorm narrow aligned rows through the flat kernels
+    int split = 0;            // wide unaligned rows through the split-row kernels (rwn_split.hpp)
     int pf = 0;               // software-pipelined tile loop: 0 off, 1 one tile ahead (cpt * rt <= 2),
                               // 2 two tiles ahead (cpt * rt == 1, vector modes)
     int base_shift = 0;       // SHIFTED: base misalignment in elements
@@ -205,6 +206,22 @@ hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const vo
                           hipStream_t s);
 // Stage 2: P partial rows of ng columns (element (p, c) at ws[p * rs + c * cs]) ->
 // out0 [N], out1 [N], out2 [1] in param dtype pdt.
+// The split-row kernels (plans with p.split set): wide rows not aligned to 16-byte chunks.
+hipError_t launch_dyt_fwd_split(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                                const void* gamma, const void* beta, void* y, hipStream_t s);
+hipError_t launch_dyt_bwd_split(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                                const void* alpha, const void* gamma, void* dx, float* ws, hipStream_t s);
+hipError_t launch_ln_fwd_split(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
+                               const void* beta, float eps, void* y, float* mean, float* rstd, hipStream_t s);
+hipError_t launch_ln_bwd_split(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                               const float* mean, const float* rstd, const void* gamma, float eps,
+                               void* dx, float* ws, hipStream_t s);
+hipError_t launch_rms_fwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
+                                float eps, void* y, float* rstd, hipStream_t s);
+hipError_t launch_rms_bwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
+                                const float* rstd, const void* w, float eps, void* dx, float* ws, hipStream_t s);
+int resident_wgs_split(int layer, bool backward, const Plan& p, int xdt, int pdt);
+
 hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
                             int64_t N, void* out0, void* out1, void* out2, hipStream_t s);
 hipError_t launch_stream_probe(const void* a, const void* b, void* out, size_t bytes, int unroll,

@@ -322,7 +322,8 @@ from tests import gpu_cases as gc
 bad = []
 for layer in ("dyt", "layernorm", "rmsnorm"):
     for (M, N, xdt, pdt) in [(4099, 24, "f32", "f32"), (1031, 128, "bf16", "f32"), (130, 2048, "bf16", "bf16"),
-                             (67, 1025, "bf16", "f32"), (33, 4096, "f32", "f32")]:
+                             (67, 1025, "bf16", "f32"), (33, 4096, "f32", "f32"), (515, 1025, "f32", "f32"),
+                             (129, 3001, "f16", "f16")]:
         wl = workloads.small(layer, M, N, xdt, pdt, seed=11)
         print("case:", wl.name, flush=True)
         bad += [str(r) for r in gc.check_workload(wl, "cuda") if not r.ok()]
@@ -332,7 +333,8 @@ print("BAD", bad, flush=True)
 
 @pytest.mark.parametrize("env", ["RWN_PREFETCH=0", "RWN_PREFETCH=1", "RWN_PREFETCH=2", "RWN_FWD_RT=4 RWN_BWD_RT=2",
                                  "RWN_WIDE_CPT=4", "RWN_BLOCKED_K=3", "RWN_XCD_REMAP=0 RWN_WG_PER_CU=2",
-                                 "RWN_FLAT=0", "RWN_XCD_REMAP=1 RWN_BLOCKED_K=2"])
+                                 "RWN_FLAT=0", "RWN_XCD_REMAP=1 RWN_BLOCKED_K=2", "RWN_SPLIT=0", "RWN_SPLIT=2",
+                                 "RWN_SPLIT_CPT=1", "RWN_SPLIT_CPT=4"])
 def test_tuning_overrides_keep_parity(env):
     """The tuning knobs change the launch plan (pipelining depth, rows per thread, chunks per
     thread, tile assignment, grid); every plan they reach must still match the oracle.  The
