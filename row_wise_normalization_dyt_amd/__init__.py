@@ -209,8 +209,11 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
                   gamma: Optional[torch.Tensor], eps: float, param_dtype: Optional[torch.dtype] = None,
                   need_param_grads: bool = True, *, dx: Optional[torch.Tensor] = None,
                   dgamma: Optional[torch.Tensor] = None, dbeta: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, need_dgamma: Optional[bool] = None,
+                  need_dbeta: Optional[bool] = None):
     """Returns (dx, dgamma, dbeta).  mean/rstd None: recomputed from x.
+    need_dgamma / need_dbeta (default: need_param_grads) select the parameter gradients; one
+    not wanted is returned as None and its column partials are never formed.
     dx=, dgamma=, dbeta=, workspace=: buffers to use instead of fresh tensors."""
     lib = _L()
     x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
@@ -226,10 +229,12 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
         if t is not None and t.dtype != torch.float32:
             raise TypeError(f"{nm} must be float32")
     dx = _out_rows(dx, x2, "dx")
-    dg = _out_vec(dgamma, N, pdtype, x2.device, "dgamma") if need_param_grads else None
-    db = _out_vec(dbeta, N, pdtype, x2.device, "dbeta") if need_param_grads else None
+    want_g = need_param_grads if need_dgamma is None else need_dgamma
+    want_b = need_param_grads if need_dbeta is None else need_dbeta
+    dg = _out_vec(dgamma, N, pdtype, x2.device, "dgamma") if want_g else None
+    db = _out_vec(dbeta, N, pdtype, x2.device, "dbeta") if want_b else None
     with torch.cuda.device(x2.device):
-        ws = _workspace("layernorm", M, N, x2.dtype, x2.device, workspace) if need_param_grads else None
+        ws = _workspace("layernorm", M, N, x2.dtype, x2.device, workspace) if (want_g or want_b) else None
         _lib.check(lib, "layernorm_bwd", lib.layernorm_bwd(M, N, _ptr(x2), _ptr(dy2), _dt(x2, "x"), _ptr(mean),
                                                            _ptr(rstd), _ptr(gamma), _DT[pdtype], float(eps),
                                                            _ptr(dx), _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),

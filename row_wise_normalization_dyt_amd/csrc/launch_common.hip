@@ -44,6 +44,7 @@ static int64_t next_pow2(int64_t v) {
 //                           kernels for unaligned wide rows and the aligned ones they measured
 //                           faster on; 2: for every wide row)
 //   RWN_SPLIT_CPT           1, 2 or 4: chunks per lane of split-row plans
+//   RWN_SPLIT_PF            0 / 1: split-row tile loop plain / one tile ahead
 static int env_int(const char* name, int lo, int hi, int dflt) {
     const char* s = getenv(name);
     if (!s) return dflt;
@@ -134,6 +135,7 @@ static void partial_layout(int layer, Plan& p) {
 static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int b, int cus,
                        bool occupancy, int wg_per_cu, int min_waves, int xcd_remap, int max_w, Plan* pp) {
     static const int split_cpt = env_int("RWN_SPLIT_CPT", 1, 4, 0);
+    static const int split_pf = env_int("RWN_SPLIT_PF", 0, 1, -1);
     Plan& p = *pp;
     const int esz = xdt == DT_F32 ? 4 : 2;
     const int V = 16 / esz;
@@ -170,7 +172,7 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     p.tpr = 64 * bw;
     p.rpp = std::max(1, kSplitBlock / p.tpr);
     p.ncb = 1;
-    p.pf = 0;
+    p.pf = split_pf >= 0 ? split_pf : 0;
     p.flat = 0;
     const int ngrad = layer == LAYER_RMS ? 1 : 2;
     if (backward && p.rpp > 1 && (int64_t)ngrad * N * 4 > 48 * 1024) p.rpp = 1;
@@ -438,17 +440,20 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
 }
 
 hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
-                            int64_t N, void* out0, void* out1, void* out2, hipStream_t s) {
+                            int64_t N, int64_t c_lo, int64_t c_hi, void* out0, void* out1, void* out2,
+                            hipStream_t s) {
+    if (c_hi > 2 * N + 1) c_hi = 2 * N + 1;   // column 2N's workgroup adds the columns after it
+    if (c_lo < 0 || c_lo >= c_hi) return hipSuccess;
     if (rs == 1) {
-        // Column-major partials: one workgroup per output column (2N + 1 of them at most).
-        const unsigned grid = (unsigned)(ng < 2 * N + 1 ? ng : 2 * N + 1);
+        // Column-major partials: one workgroup per output column.
+        const unsigned grid = (unsigned)(c_hi - c_lo);
         if (pdt == DT_F32)
-            return launch(colreduce_cm_kernel<float>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+            return launch(colreduce_cm_kernel<float>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N, c_lo,
                           (float*)out0, (float*)out1, (float*)out2);
         if (pdt == DT_F16)
-            return launch(colreduce_cm_kernel<f16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+            return launch(colreduce_cm_kernel<f16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N, c_lo,
                           (f16_t*)out0, (f16_t*)out1, (f16_t*)out2);
-        return launch(colreduce_cm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N,
+        return launch(colreduce_cm_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, ws, P, ng, cs, N, c_lo,
                       (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
     }
     const int block = 512;
@@ -460,16 +465,16 @@ hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int
     if (L < 8) L = 8;
     if (L > lmax) L = lmax;
     const int cb = (int)(block / L);
-    const unsigned grid = (unsigned)((ng + cb - 1) / cb);
+    const unsigned grid = (unsigned)((c_hi - c_lo + cb - 1) / cb);
     if (pdt == DT_F32) {
-        return launch(colreduce_kernel<float>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
-                      (float*)out0, (float*)out1, (float*)out2);
+        return launch(colreduce_kernel<float>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, c_lo, c_hi,
+                      cb, (float*)out0, (float*)out1, (float*)out2);
     } else if (pdt == DT_F16) {
-        return launch(colreduce_kernel<f16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
-                      (f16_t*)out0, (f16_t*)out1, (f16_t*)out2);
+        return launch(colreduce_kernel<f16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, c_lo, c_hi,
+                      cb, (f16_t*)out0, (f16_t*)out1, (f16_t*)out2);
     } else {
-        return launch(colreduce_kernel<bf16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, cb,
-                      (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
+        return launch(colreduce_kernel<bf16_t>, dim3(grid), dim3(block), 0, s, ws, P, ng, rs, cs, N, c_lo, c_hi,
+                      cb, (bf16_t*)out0, (bf16_t*)out1, (bf16_t*)out2);
     }
 }
 

@@ -38,11 +38,11 @@ hipError_t launch_ln_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, co
 
 hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                               const float* mean, const float* rstd, const void* gamma, float eps,
-                              void* dx, float* ws, hipStream_t s) {
+                              void* dx, float* ws, int grads, hipStream_t s) {
     if (p.block > 256 || p.block < 1) return hipErrorInvalidConfiguration;
     const Geom g = make_geom(p);
     const bool st = mean != nullptr && rstd != nullptr;
-    return dispatch_pg(ws, [&](auto pg) {
+    return dispatch_ln_grads(ws, grads, [&](auto pg) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
@@ -63,7 +63,7 @@ int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt) {
         using PT = typename decltype(pt)::type;
         return dispatch_tpr(p, [&](auto tpr) {
             constexpr int R = decltype(tpr)::value;
-            const void* k = backward ? (const void*)ln_bwd_flat_kernel<T, PT, R, 1, 1>
+            const void* k = backward ? (const void*)ln_bwd_flat_kernel<T, PT, R, 3, 1>
                                      : (const void*)ln_fwd_flat_kernel<T, PT, R>;
             n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
             return hipSuccess;

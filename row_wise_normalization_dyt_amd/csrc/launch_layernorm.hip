@@ -1,4 +1,5 @@
-// LayerNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT, prefetch).
+// LayerNorm launchers: forward and backward stage 1 for every (dtype pair, mode, CPT, RT, prefetch,
+// requested parameter gradients).
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -26,11 +27,11 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
 
 hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                          const float* mean, const float* rstd, const void* gamma, float eps,
-                         void* dx, float* ws, hipStream_t s) {
+                         void* dx, float* ws, int grads, hipStream_t s) {
     const Geom g = make_geom(p);
-    if (p.split) return launch_ln_bwd_split(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, s);
-    if (p.flat) return launch_ln_bwd_flat(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, s);
-    return dispatch_pg(ws, [&](auto pg) {
+    if (p.split) return launch_ln_bwd_split(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, grads, s);
+    if (p.flat) return launch_ln_bwd_flat(p, xdt, pdt, x, dy, mean, rstd, gamma, eps, dx, ws, grads, s);
+    return dispatch_ln_grads(ws, grads, [&](auto pg) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
@@ -57,7 +58,7 @@ int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt) {
             {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
                 constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
-                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_, 1>
+                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_, 3>
                                          : (const void*)ln_fwd_kernel<T, PT, M_, C_, R_, P_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;

@@ -189,12 +189,15 @@ rwn_status check_workspace(const char* fn, const Plan& p, int layer, const void*
     return RWN_OK;
 }
 
-// Stage 2 (also the whole backward when M == 0: P = 0 partial rows give zeros).
+// Stage 2 (also the whole backward when M == 0: P = 0 partial rows give zeros).  Reads only
+// the columns from the first requested output's to the last's.
 rwn_status finish_bwd(const char* fn, int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs,
                       int64_t cs, int64_t N, void* out0, void* out1, void* out2, hipStream_t s) {
     if (!out0 && !out1 && !out2) return ok();
+    const int64_t c_lo = out0 ? 0 : out1 ? N : 2 * N;
+    const int64_t c_hi = out2 ? ng : out1 ? 2 * N : N;
     hipError_t e = traced(RWN_K_COLREDUCE, s, [&] {
-        return launch_colreduce(pdt, ws, P, ng, rs, cs, N, out0, out1, out2, s);
+        return launch_colreduce(pdt, ws, P, ng, rs, cs, N, c_lo, c_hi, out0, out1, out2, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -335,8 +338,10 @@ rwn_status ln_bwd_impl(const char* fn, int64_t M, int64_t N, const void* x, cons
     if ((st = check_operands(fn, x_dtype, ops, names, 3, &mis)) != RWN_OK) return st;
     Plan p;
     if ((st = plan_for(fn, LAYER_LN, true, M, N, x_dtype, param_dtype, mis, &p)) != RWN_OK) return st;
-    // No parameter gradient wanted: dx only, no workspace, no stage 2.
+    // No parameter gradient wanted: dx only, no workspace, no stage 2.  Otherwise stage 1 writes
+    // the partial columns of the requested gradients only.
     const bool grads = dgamma || dbeta;
+    const int mask = (dgamma ? 1 : 0) | (dbeta ? 2 : 0);
     float* ws = nullptr;
     if (grads && static_scratch) {
         const size_t need = (size_t)p.partial_rows() * (size_t)ng * sizeof(float);
@@ -351,7 +356,7 @@ rwn_status ln_bwd_impl(const char* fn, int64_t M, int64_t N, const void* x, cons
         ws = (float*)workspace;
     }
     hipError_t e = traced(RWN_K_LN_BWD, s, [&] {
-        return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, s);
+        return launch_ln_bwd(p, x_dtype, param_dtype, x, dy, mean, rstd, gamma, eps, dx, ws, mask, s);
     });
     if (e != hipSuccess) return hip_fail(e, fn);
     return finish_bwd(fn, param_dtype, ws, p.partial_rows(), ng, p.ws_rs, p.ws_cs, N, dgamma, dbeta, nullptr, s);

@@ -484,6 +484,8 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
     tile_loop<PF, In>(c, fetch, body);
 }
 
+// PG: which parameter-gradient partials are accumulated and written (bit 0: dgamma, bit 1:
+// dbeta; 0: dx only, the workspace may be NULL).
 template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
@@ -576,10 +578,8 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     const int e = k * V + v;
                     const float gv = gr[u].get(k, v);
                     const float xh = (xr[u].get(k, v) - mu[u]) * rs[u];
-                    if constexpr (PG) {
-                        acc_g[e] = __builtin_fmaf(gv, xh, acc_g[e]);
-                        acc_b[e] += gv;
-                    }
+                    if constexpr (PG & 1) acc_g[e] = __builtin_fmaf(gv, xh, acc_g[e]);
+                    if constexpr (PG & 2) acc_b[e] += gv;
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
                 put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
@@ -587,11 +587,10 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         }
     };
     tile_loop<PF, In>(c, fetch, body);
-    if constexpr (PG) {
-        float* out = ws + c.wg * g.ws_rs;
-        write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+    float* out = ws + c.wg * g.ws_rs;
+    if constexpr (PG & 1) write_partial<T, MODE, CPT>(out, g.ws_cs, acc_g, c.cm, c.slot, c.lane, g, part);
+    if constexpr (PG & 2)
         write_partial<T, MODE, CPT>(out + g.N * g.ws_cs, g.ws_cs, acc_b, c.cm, c.slot, c.lane, g, part);
-    }
 }
 
 // ------------------------------------------------------------ LayerNorm, flat narrow rows
@@ -654,22 +653,24 @@ struct FlatCtx {
     }
 };
 
-// Both LayerNorm partial rows of a flat workgroup (dgamma at out_g, dbeta at out_b, column
-// stride cs) in one combine: the two gradients' butterflies interleave and share one LDS round,
-// so the workgroup's tail pays the latency once.  The order is write_partial's for narrow rows:
-// an xor butterfly over the wave's row slots, then the waves' sums in wave order.
-template <typename T, int TPR>
+// The requested LayerNorm partial rows of a flat workgroup (PG bit 0: dgamma at out_g, bit 1:
+// dbeta at out_b, column stride cs) in one combine: the gradients' butterflies interleave and
+// share one LDS round, so the workgroup's tail pays the latency once.  The order is
+// write_partial's for narrow rows: an xor butterfly over the wave's row slots, then the waves'
+// sums in wave order.
+template <typename T, int TPR, int PG>
 __device__ __forceinline__ void write_partial_pair(float* __restrict__ out_g, float* __restrict__ out_b,
                                                    int64_t cs, const float* acc_g, const float* acc_b,
                                                    int lane, bool lane_in, int64_t col, float* part) {
     constexpr int V = Elems<T, MODE_ALIGNED>::value;
-    constexpr int E = 2 * V;
+    constexpr int NGR = ((PG & 1) ? 1 : 0) + ((PG & 2) ? 1 : 0);
+    constexpr int E = NGR * V;
     const int nb = blockDim.x;
     float v[E];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        v[e] = acc_g[e];
-        v[V + e] = acc_b[e];
+        if constexpr (PG & 1) v[e] = acc_g[e];
+        if constexpr (PG & 2) v[(PG & 1 ? V : 0) + e] = acc_b[e];
     }
     if constexpr (TPR < 64) {
         const int wl = nb < 64 ? nb : 64;
@@ -691,8 +692,9 @@ __device__ __forceinline__ void write_partial_pair(float* __restrict__ out_g, fl
         for (int e = 0; e < E; ++e) {
             float sum = part[lane * E + e];
             for (int w = 1; w < nw; ++w) sum += part[(w * TPR + lane) * E + e];
-            if (e < V) out_g[(col + e) * cs] = sum;
-            else out_b[(col + e - V) * cs] = sum;
+            const bool to_g = (PG & 1) && e < V;
+            if (to_g) out_g[(col + e) * cs] = sum;
+            else out_b[(col + e - ((PG & 1) ? V : 0)) * cs] = sum;
         }
     }
 }
@@ -792,19 +794,17 @@ ln_bwd_flat_kernel(const T* __restrict__ x, const T* __restrict__ dy, const floa
         for (int v = 0; v < V; ++v) {
             const float gv = gr.get(0, v);
             const float xh = (xr.get(0, v) - mu) * rs;
-            if constexpr (PG) {
-                acc_g[v] = __builtin_fmaf(gv, xh, acc_g[v]);
-                acc_b[v] += gv;
-            }
+            if constexpr (PG & 1) acc_g[v] = __builtin_fmaf(gv, xh, acc_g[v]);
+            if constexpr (PG & 2) acc_b[v] += gv;
             o[v] = rs * (gv * ga[v] - c1 - xh * c2);
         }
         if (ok && lane_in)
             __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(dx + row * g.N + col));
     }
-    if constexpr (PG) {
+    if constexpr (PG != 0) {
         float* out = ws + c.wg * g.ws_rs;
-        write_partial_pair<T, TPR>(out, out + g.N * g.ws_cs, g.ws_cs, acc_g, acc_b, c.lane, c.lane_in,
-                                   c.col, part);
+        write_partial_pair<T, TPR, PG>(out, out + g.N * g.ws_cs, g.ws_cs, acc_g, acc_b, c.lane, c.lane_in,
+                                       c.col, part);
     }
 }
 
@@ -1008,15 +1008,15 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
 // ============================================================================ stage 2
 
 // Stage 2.  Partial row p, column c is ws[p * rs + c * cs].  Output columns: [0, N) -> out0,
-// [N, 2N) -> out1, 2N -> out2[0] (NULL outputs are skipped).  A workgroup covers cb columns
-// with L = blockDim.x / cb lanes each; lane l adds partial rows l, l + L, ... in order in
+// [N, 2N) -> out1, 2N -> out2[0] (NULL outputs are skipped); only columns [c_lo, c_hi) are
+// read.  A workgroup covers cb columns with L = blockDim.x / cb lanes each; lane l adds partial rows l, l + L, ... in order in
 // float64, then the L lane sums are added as a fixed tree.  Threads are laid out along the
 // contiguous dimension of ws (columns when cs == 1, partial rows otherwise) so loads coalesce.
 template <typename PT>
 __global__ void __launch_bounds__(512)
 colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
-                 int64_t N, int cb, PT* __restrict__ out0, PT* __restrict__ out1,
-                 PT* __restrict__ out2) {
+                 int64_t N, int64_t c_lo, int64_t c_hi, int cb, PT* __restrict__ out0,
+                 PT* __restrict__ out1, PT* __restrict__ out2) {
     // Columns [2N, ng) are the dalpha partial columns of the column blocks: the lanes of column
     // 2N add all of them (column by column, in order); the others stay idle.
     __shared__ double red[512];
@@ -1024,10 +1024,11 @@ colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs
     const bool col_fast = cs == 1;
     const int cl = col_fast ? (int)(threadIdx.x % cb) : (int)(threadIdx.x / L);
     const int gl = col_fast ? (int)(threadIdx.x / cb) : (int)(threadIdx.x % L);
-    const int64_t col = (int64_t)blockIdx.x * cb + cl;
+    const int64_t col = c_lo + (int64_t)blockIdx.x * cb + cl;
+    const bool live = col < c_hi && col < ng && col <= 2 * N;
     double acc = 0.0;
     const int64_t c_end = col == 2 * N ? ng : col + 1;
-    if (col < ng && col <= 2 * N) {
+    if (live) {
         for (int64_t cc = col; cc < c_end; ++cc) {
             const float* base = ws + cc * cs;
             int64_t p = gl;
@@ -1045,7 +1046,7 @@ colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs
         if (gl < st) red[gl * cb + cl] += red[(gl + st) * cb + cl];
         __syncthreads();
     }
-    if (gl == 0 && col < ng && col <= 2 * N) {
+    if (gl == 0 && live) {
         const PT v = from_f32<PT>((float)red[cl]);
         if (col < N) {
             if (out0) out0[col] = v;
@@ -1058,16 +1059,16 @@ colreduce_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t rs
 }
 
 // Stage 2 for column-major partials (rs == 1: column c is ws[c * cs .. c * cs + P)), the
-// layout of short rows.  One workgroup per output column: thread t adds partial rows t,
+// layout of short rows.  One workgroup per output column from c_lo on: thread t adds partial rows t,
 // t + blockDim, ... in order in float64 (all of its loads issued up front), the wave sums
 // are formed by a fixed xor butterfly, and thread 0 adds the wave sums in wave order.  The
 // dalpha output (column 2N) adds its ncb partial columns [2N, ng) one after another.
 template <typename PT>
 __global__ void __launch_bounds__(256)
 colreduce_cm_kernel(const float* __restrict__ ws, int64_t P, int64_t ng, int64_t cs, int64_t N,
-                    PT* __restrict__ out0, PT* __restrict__ out1, PT* __restrict__ out2) {
+                    int64_t c_lo, PT* __restrict__ out0, PT* __restrict__ out1, PT* __restrict__ out2) {
     __shared__ double wsum[4];
-    const int64_t col = blockIdx.x;
+    const int64_t col = c_lo + blockIdx.x;
     const int64_t c_end = col == 2 * N ? ng : col + 1;
     double acc = 0.0;
     for (int64_t cc = col; cc < c_end; ++cc) {

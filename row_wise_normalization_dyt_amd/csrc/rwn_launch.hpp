@@ -101,6 +101,19 @@ hipError_t dispatch_pg(const float* ws, F&& f) {
     return ws ? f(IC<1>{}) : f(IC<0>{});
 }
 
+// LayerNorm's gradient selection as a template value: bit 0 dgamma, bit 1 dbeta (no workspace:
+// dx only, whatever the mask says).
+template <typename F>
+hipError_t dispatch_ln_grads(const float* ws, int grads, F&& f) {
+    if (!ws) return f(IC<0>{});
+    switch (grads & 3) {
+    case 1: return f(IC<1>{});
+    case 2: return f(IC<2>{});
+    case 3: return f(IC<3>{});
+    default: return f(IC<0>{});
+    }
+}
+
 // Calls f(TypeTag<T>, TypeTag<PT>) for the supported dtype pairs.
 template <typename F>
 hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
@@ -186,14 +199,14 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
                          hipStream_t s);
 hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                          const float* mean, const float* rstd, const void* gamma, float eps,
-                         void* dx, float* ws, hipStream_t s);
+                         void* dx, float* ws, int grads, hipStream_t s);
 // The flat LayerNorm kernels of narrow aligned rows (plans with p.flat set).
 hipError_t launch_ln_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
                               const void* beta, float eps, void* y, float* mean, float* rstd,
                               hipStream_t s);
 hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                               const float* mean, const float* rstd, const void* gamma, float eps,
-                              void* dx, float* ws, hipStream_t s);
+                              void* dx, float* ws, int grads, hipStream_t s);
 int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt);
 // RMSNorm forms: the Llama form rounds the normalized value to x's dtype before the weight
 // multiply; the two others multiply in float32 and round once, by weight or by (1 + weight).
@@ -215,15 +228,19 @@ hipError_t launch_ln_fwd_split(const Plan& p, int xdt, int pdt, const void* x, c
                                const void* beta, float eps, void* y, float* mean, float* rstd, hipStream_t s);
 hipError_t launch_ln_bwd_split(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
                                const float* mean, const float* rstd, const void* gamma, float eps,
-                               void* dx, float* ws, hipStream_t s);
+                               void* dx, float* ws, int grads, hipStream_t s);
 hipError_t launch_rms_fwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                                 float eps, void* y, float* rstd, hipStream_t s);
 hipError_t launch_rms_bwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
                                 const float* rstd, const void* w, float eps, void* dx, float* ws, hipStream_t s);
 int resident_wgs_split(int layer, bool backward, const Plan& p, int xdt, int pdt);
 
+// Stage 2: sums the P partial rows of columns [c_lo, c_hi) (column c at ws + c * cs, partial
+// row p at + p * rs) into out0 (columns [0, N)), out1 ([N, 2N)) and out2 (column 2N, which also
+// takes the columns after it).  Only the requested gradients' columns are read.
 hipError_t launch_colreduce(int pdt, const float* ws, int64_t P, int64_t ng, int64_t rs, int64_t cs,
-                            int64_t N, void* out0, void* out1, void* out2, hipStream_t s);
+                            int64_t N, int64_t c_lo, int64_t c_hi, void* out0, void* out1, void* out2,
+                            hipStream_t s);
 hipError_t launch_stream_probe(const void* a, const void* b, void* out, size_t bytes, int unroll,
                                int nontemporal, int wg_per_cu, int cus, hipStream_t s);
 

@@ -17,10 +17,12 @@
 //
 // Loads are plain nontemporal global loads; an unused chunk or scalar slot (or a row past M)
 // loads an aligned chunk known to lie inside the tensor and is zeroed after the load, so no load
-// sits behind a branch.  The arithmetic is the general kernels'; only the row is cut differently.
+// sits behind a branch.  PF = 1 issues the next tile's loads before the current tile is reduced,
+// computed and stored (tile_loop).  The arithmetic is the general kernels'; only the row is cut
+// differently.
 #pragma once
 
-#include "rwn_device.hpp"
+#include "rwn_kernels.hpp"
 
 namespace rwn {
 
@@ -32,7 +34,7 @@ template <typename T, int CPT>
 struct SplitCtx {
     static constexpr int V = ChunkOf<T>::value;
     int slot, lane;
-    int64_t t_begin, t_step;   // this workgroup's tiles: t_begin, t_begin + t_step, ...
+    int64_t t_begin, t_end, t_step;   // this workgroup's tiles: t_begin, t_begin + t_step, ... < t_end
     int64_t wg;                // its partial row (backward)
     int h, nm, nrem;           // head elements, main chunks, head + tail elements
     int col[CPT];              // column of element 0 of main chunk k
@@ -48,6 +50,7 @@ struct SplitCtx {
         if (g.xcd_remap) b = (b % 8) * (gridDim.x / 8) + b / 8;
         wg = b;
         t_begin = b;
+        t_end = g.ntiles;
         t_step = gridDim.x;
         const int64_t r0 = t_begin * g.rpp + slot;
         const int s = (int)(((int64_t)g.base_shift + r0 * g.N) % V);
@@ -186,7 +189,23 @@ __device__ __forceinline__ void split_write_partials(float* __restrict__ out, in
 
 // ================================================================================== DyT
 
-template <typename T, typename PT, int CPT>
+// Row of the tile for this slot, whether it exists (and the tile is one of this workgroup's),
+// and its first element.
+struct SplitRowPos {
+    int64_t row, e0;
+    bool rv;
+};
+
+template <typename T, int CPT>
+__device__ __forceinline__ SplitRowPos split_pos(const SplitCtx<T, CPT>& c, int64_t tile, const Geom& g) {
+    SplitRowPos r;
+    r.row = c.row(tile, g);
+    r.rv = tile < c.t_end && r.row < g.M;
+    r.e0 = r.row * g.N;
+    return r;
+}
+
+template <typename T, typename PT, int CPT, int PF>
 __global__ void __launch_bounds__(kSplitBlock)
 dyt_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
                      const PT* __restrict__ beta, T* __restrict__ y, Geom g) {
@@ -197,24 +216,28 @@ dyt_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p, co
     split_param<T, PT, CPT>(gamma, 0.f, c, ga, gs);
     split_param<T, PT, CPT>(beta, 0.f, c, be, bs);
     const float alpha = to_f32(alpha_p[0]);
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    struct In {
         SplitRow<T, CPT> xr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
+        SplitRowPos at;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+    };
+    auto body = [&](const In& in) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float o[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * xr.get(k, v)), be[k * V + v]);
-            split_store_chunk<T, CPT>(y, e0, c, k, o, rv);
+            for (int v = 0; v < V; ++v) o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * in.xr.get(k, v)), be[k * V + v]);
+            split_store_chunk<T, CPT>(y, in.at.e0, c, k, o, in.at.rv);
         }
-        split_store_scalar<T, CPT>(y, e0, c, __builtin_fmaf(gs, tanh_only(alpha * xr.gets()), bs), rv);
-    }
+        split_store_scalar<T, CPT>(y, in.at.e0, c, __builtin_fmaf(gs, tanh_only(alpha * in.xr.gets()), bs), in.at.rv);
+    };
+    tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int CPT, int PG>
+template <typename T, typename PT, int CPT, int PF, int PG>
 __global__ void __launch_bounds__(kSplitBlock)
 dyt_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
                      const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws, Geom g) {
@@ -255,30 +278,35 @@ dyt_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT
             return d * as;
         }
     };
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    struct In {
         SplitRow<T, CPT> xr, gr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
-        split_load<T, CPT>(dy, e0, c, rv, gr);
-        auto body = [&](auto fin) {
+        SplitRowPos at;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+        split_load<T, CPT>(dy, in.at.e0, c, in.at.rv, in.gr);
+    };
+    auto body = [&](const In& in) {
+        const bool rv = in.at.rv;
+        auto rows = [&](auto fin) {
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
                 float o[V];
                 const bool live = rv && c.ok[k];
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    o[v] = elem(fin, xr.get(k, v), gr.get(k, v), ga[k * V + v], live, acc[0][k * V + v],
+                    o[v] = elem(fin, in.xr.get(k, v), in.gr.get(k, v), ga[k * V + v], live, acc[0][k * V + v],
                                 acc[1][k * V + v]);
-                split_store_chunk<T, CPT>(dx, e0, c, k, o, rv);
+                split_store_chunk<T, CPT>(dx, in.at.e0, c, k, o, rv);
             }
-            const float os = elem(fin, xr.gets(), gr.gets(), gs, rv && c.sok, accs[0], accs[1]);
-            split_store_scalar<T, CPT>(dx, e0, c, os, rv);
+            const float os = elem(fin, in.xr.gets(), in.gr.gets(), gs, rv && c.sok, accs[0], accs[1]);
+            split_store_scalar<T, CPT>(dx, in.at.e0, c, os, rv);
         };
-        if (finite_alpha) body(IC<1>{});
-        else body(IC<0>{});
-    }
+        if (finite_alpha) rows(IC<1>{});
+        else rows(IC<0>{});
+    };
+    tile_loop<PF, In>(c, fetch, body);
     if constexpr (PG) {
         float* out = ws + c.wg * g.ws_rs;
         split_write_partials<T, CPT, 2>(out, g.ws_cs, acc, accs, c, g, part);
@@ -318,7 +346,7 @@ __device__ __forceinline__ void split_ln_stats(const SplitRow<T, CPT>& xr, const
     rs = __builtin_amdgcn_rsqf(s[0] * g.inv_n + eps);
 }
 
-template <typename T, typename PT, int CPT>
+template <typename T, typename PT, int CPT, int PF>
 __global__ void __launch_bounds__(kSplitBlock)
 ln_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta, float eps,
                     T* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out, Geom g) {
@@ -330,30 +358,35 @@ ln_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const
     float ga[E], be[E], gs, bs;
     split_param<T, PT, CPT>(gamma, 1.f, c, ga, gs);
     split_param<T, PT, CPT>(beta, 0.f, c, be, bs);
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    struct In {
         SplitRow<T, CPT> xr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
+        SplitRowPos at;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+    };
+    auto body = [&](const In& in) {
         float mu, rs;
-        split_ln_stats<T, CPT>(xr, c, g, eps, red, parity, mu, rs);
+        split_ln_stats<T, CPT>(in.xr, c, g, eps, red, parity, mu, rs);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float o[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) o[v] = __builtin_fmaf((xr.get(k, v) - mu) * rs, ga[k * V + v], be[k * V + v]);
-            split_store_chunk<T, CPT>(y, e0, c, k, o, rv);
+            for (int v = 0; v < V; ++v)
+                o[v] = __builtin_fmaf((in.xr.get(k, v) - mu) * rs, ga[k * V + v], be[k * V + v]);
+            split_store_chunk<T, CPT>(y, in.at.e0, c, k, o, in.at.rv);
         }
-        split_store_scalar<T, CPT>(y, e0, c, __builtin_fmaf((xr.gets() - mu) * rs, gs, bs), rv);
-        if (rv && c.lane == 0) {
-            if (mean_out) mean_out[row] = mu;
-            if (rstd_out) rstd_out[row] = rs;
+        split_store_scalar<T, CPT>(y, in.at.e0, c, __builtin_fmaf((in.xr.gets() - mu) * rs, gs, bs), in.at.rv);
+        if (in.at.rv && c.lane == 0) {
+            if (mean_out) mean_out[in.at.row] = mu;
+            if (rstd_out) rstd_out[in.at.row] = rs;
         }
-    }
+    };
+    tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int CPT, int PG>
+template <typename T, typename PT, int CPT, int PF, int PG>
 __global__ void __launch_bounds__(kSplitBlock)
 ln_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
                     const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
@@ -367,38 +400,48 @@ ln_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const flo
     float ga[E], gs;
     split_param<T, PT, CPT>(gamma, 1.f, c, ga, gs);
     const bool have_stats = mean_in != nullptr && rstd_in != nullptr;
-    float acc[2][E], accs[2] = {0.f, 0.f};
+    // PG bit 0: dgamma partials (acc[0]), bit 1: dbeta partials (acc[IB])
+    constexpr int NGR = (PG & 1) + ((PG >> 1) & 1) > 0 ? (PG & 1) + ((PG >> 1) & 1) : 1;
+    constexpr int IB = (PG & 1) ? 1 : 0;
+    float acc[NGR][E], accs[NGR];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[0][e] = acc[1][e] = 0.f;
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    for (int n = 0; n < NGR; ++n) {
+        accs[n] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[n][e] = 0.f;
+    }
+    struct In {
         SplitRow<T, CPT> xr, gr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
-        split_load<T, CPT>(dy, e0, c, rv, gr);
-        float mu = 0.f, rs = 0.f;
-        if (have_stats) {
-            mu = mean_in[rv ? row : 0];
-            rs = rstd_in[rv ? row : 0];
-        } else {
-            split_ln_stats<T, CPT>(xr, c, g, eps, red, parity, mu, rs);
-        }
+        SplitRowPos at;
+        float mu, rs;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+        split_load<T, CPT>(dy, in.at.e0, c, in.at.rv, in.gr);
+        const int64_t sr = in.at.rv ? in.at.row : 0;
+        in.mu = have_stats ? mean_in[sr] : 0.f;
+        in.rs = have_stats ? rstd_in[sr] : 0.f;
+    };
+    auto body = [&](const In& in) {
+        const bool rv = in.at.rv;
+        float mu = in.mu, rs = in.rs;
+        if (!have_stats) split_ln_stats<T, CPT>(in.xr, c, g, eps, red, parity, mu, rs);
         // A row past M adds nothing: its dy is 0 and its statistics are zeroed (recomputed ones
         // are infinite with eps = 0).  Unused slots have dy = gamma = 0, so every term is 0.
         mu = rv ? mu : 0.f;
         rs = rv ? rs : 0.f;
         float s[2];
         {
-            const float xh = (xr.gets() - mu) * rs;
-            const float gg = gr.gets() * gs;
+            const float xh = (in.xr.gets() - mu) * rs;
+            const float gg = in.gr.gets() * gs;
             float a = gg, b = gg * xh;
 #pragma unroll
             for (int k = 0; k < CPT; ++k)
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    const float xh2 = (xr.get(k, v) - mu) * rs;
-                    const float gg2 = gr.get(k, v) * ga[k * V + v];
+                    const float xh2 = (in.xr.get(k, v) - mu) * rs;
+                    const float gg2 = in.gr.get(k, v) * ga[k * V + v];
                     a += gg2;
                     b = __builtin_fmaf(gg2, xh2, b);
                 }
@@ -413,27 +456,27 @@ ln_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const flo
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int e = k * V + v;
-                const float gv = gr.get(k, v);
-                const float xh = (xr.get(k, v) - mu) * rs;
-                if constexpr (PG) {
-                    acc[0][e] = __builtin_fmaf(gv, xh, acc[0][e]);
-                    acc[1][e] += gv;
-                }
+                const float gv = in.gr.get(k, v);
+                const float xh = (in.xr.get(k, v) - mu) * rs;
+                if constexpr (PG & 1) acc[0][e] = __builtin_fmaf(gv, xh, acc[0][e]);
+                if constexpr (PG & 2) acc[IB][e] += gv;
                 o[v] = rs * (gv * ga[e] - c1 - xh * c2);
             }
-            split_store_chunk<T, CPT>(dx, e0, c, k, o, rv);
+            split_store_chunk<T, CPT>(dx, in.at.e0, c, k, o, rv);
         }
         {
-            const float gv = gr.gets();
-            const float xh = (xr.gets() - mu) * rs;
-            if constexpr (PG) {
-                accs[0] = __builtin_fmaf(gv, xh, accs[0]);
-                accs[1] += gv;
-            }
-            split_store_scalar<T, CPT>(dx, e0, c, rs * (gv * gs - c1 - xh * c2), rv);
+            const float gv = in.gr.gets();
+            const float xh = (in.xr.gets() - mu) * rs;
+            if constexpr (PG & 1) accs[0] = __builtin_fmaf(gv, xh, accs[0]);
+            if constexpr (PG & 2) accs[IB] += gv;
+            split_store_scalar<T, CPT>(dx, in.at.e0, c, rs * (gv * gs - c1 - xh * c2), rv);
         }
-    }
-    if constexpr (PG) split_write_partials<T, CPT, 2>(ws + c.wg * g.ws_rs, g.ws_cs, acc, accs, c, g, part);
+    };
+    tile_loop<PF, In>(c, fetch, body);
+    // the requested gradients are adjacent in [dgamma | dbeta]: dbeta alone starts at column N
+    if constexpr (PG != 0)
+        split_write_partials<T, CPT, NGR>(ws + c.wg * g.ws_rs + (PG == 2 ? g.N * g.ws_cs : 0), g.ws_cs, acc, accs,
+                                          c, g, part);
 }
 
 // ============================================================================== RMSNorm
@@ -457,7 +500,7 @@ __device__ __forceinline__ float split_rms_rstd(const SplitRow<T, CPT>& xr, cons
 }
 
 // VAR 0: the Llama form; VAR 1: weight (plus g.w_offset) times the float32 normalized value.
-template <typename T, typename PT, int CPT, int VAR>
+template <typename T, typename PT, int CPT, int PF, int VAR>
 __global__ void __launch_bounds__(kSplitBlock)
 rms_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps, T* __restrict__ y,
                      float* __restrict__ rstd_out, Geom g) {
@@ -477,26 +520,30 @@ rms_fwd_split_kernel(const T* __restrict__ x, const PT* __restrict__ weight, flo
         const float h = xv * rs;
         return wv * (VAR == 0 ? round_through<T>(h) : h);
     };
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    struct In {
         SplitRow<T, CPT> xr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
-        const float rs = split_rms_rstd<T, CPT>(xr, g, eps, red, parity);
+        SplitRowPos at;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+    };
+    auto body = [&](const In& in) {
+        const float rs = split_rms_rstd<T, CPT>(in.xr, g, eps, red, parity);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float o[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) o[v] = out(xr.get(k, v), rs, w[k * V + v]);
-            split_store_chunk<T, CPT>(y, e0, c, k, o, rv);
+            for (int v = 0; v < V; ++v) o[v] = out(in.xr.get(k, v), rs, w[k * V + v]);
+            split_store_chunk<T, CPT>(y, in.at.e0, c, k, o, in.at.rv);
         }
-        split_store_scalar<T, CPT>(y, e0, c, out(xr.gets(), rs, ws_), rv);
-        if (rv && c.lane == 0 && rstd_out) rstd_out[row] = rs;
-    }
+        split_store_scalar<T, CPT>(y, in.at.e0, c, out(in.xr.gets(), rs, ws_), in.at.rv);
+        if (in.at.rv && c.lane == 0 && rstd_out) rstd_out[in.at.row] = rs;
+    };
+    tile_loop<PF, In>(c, fetch, body);
 }
 
-template <typename T, typename PT, int CPT, int VAR, int PG>
+template <typename T, typename PT, int CPT, int PF, int VAR, int PG>
 __global__ void __launch_bounds__(kSplitBlock)
 rms_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
                      const PT* __restrict__ weight, float eps, T* __restrict__ dx, float* __restrict__ ws, Geom g) {
@@ -521,52 +568,59 @@ rms_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const fl
         const float p = gv * wv;
         return VAR == 0 ? round_through<T>(p) : p;
     };
-    for (int64_t tile = c.t_begin; tile < g.ntiles; tile += c.t_step) {
-        const int64_t row = c.row(tile, g);
-        const bool rv = row < g.M;
-        const int64_t e0 = row * g.N;
+    // weight-gradient term: Llama form dy * n (n = h rounded to x's dtype), the product rounded to
+    // the weight's dtype; float32 forms dy * h
+    auto term = [&](float gv, float h) {
+        return VAR == 0 ? round_through<PT>(gv * round_through<T>(h)) : gv * h;
+    };
+    struct In {
         SplitRow<T, CPT> xr, gr;
-        split_load<T, CPT>(x, e0, c, rv, xr);
-        split_load<T, CPT>(dy, e0, c, rv, gr);
-        float rs = rstd_in ? rstd_in[rv ? row : 0] : split_rms_rstd<T, CPT>(xr, g, eps, red, parity);
+        SplitRowPos at;
+        float rs;
+    };
+    auto fetch = [&](int64_t tile, In& in) {
+        in.at = split_pos(c, tile, g);
+        split_load<T, CPT>(x, in.at.e0, c, in.at.rv, in.xr);
+        split_load<T, CPT>(dy, in.at.e0, c, in.at.rv, in.gr);
+        in.rs = rstd_in ? rstd_in[in.at.rv ? in.at.row : 0] : 0.f;
+    };
+    auto body = [&](const In& in) {
+        const bool rv = in.at.rv;
+        float rs = rstd_in ? in.rs : split_rms_rstd<T, CPT>(in.xr, g, eps, red, parity);
         rs = rv ? rs : 0.f;   // a row past M adds nothing (a recomputed rstd is infinite with eps = 0)
         float s[1];
         {
-            float a = grad_n(gr.gets(), wsc) * (xr.gets() * rs);
+            float a = grad_n(in.gr.gets(), wsc) * (in.xr.gets() * rs);
 #pragma unroll
             for (int k = 0; k < CPT; ++k)
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    a = __builtin_fmaf(grad_n(gr.get(k, v), w[k * V + v]), xr.get(k, v) * rs, a);
+                    a = __builtin_fmaf(grad_n(in.gr.get(k, v), w[k * V + v]), in.xr.get(k, v) * rs, a);
             s[0] = a;
         }
         row_sum<1>(s, g.tpr, red, parity);
         const float cc = s[0] * g.inv_n;
-        // weight-gradient term: Llama form dy * n (n = h rounded to x's dtype), the product
-        // rounded to the weight's dtype; float32 forms dy * h
-        auto term = [&](float gv, float h) {
-            return VAR == 0 ? round_through<PT>(gv * round_through<T>(h)) : gv * h;
-        };
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float o[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const int e = k * V + v;
-                const float gv = gr.get(k, v);
-                const float h = xr.get(k, v) * rs;
+                const float gv = in.gr.get(k, v);
+                const float h = in.xr.get(k, v) * rs;
                 if constexpr (PG) acc[0][e] += term(gv, h);
                 o[v] = rs * (grad_n(gv, w[e]) - h * cc);
             }
-            split_store_chunk<T, CPT>(dx, e0, c, k, o, rv);
+            split_store_chunk<T, CPT>(dx, in.at.e0, c, k, o, rv);
         }
         {
-            const float gv = gr.gets();
-            const float h = xr.gets() * rs;
+            const float gv = in.gr.gets();
+            const float h = in.xr.gets() * rs;
             if constexpr (PG) accs[0] += term(gv, h);
-            split_store_scalar<T, CPT>(dx, e0, c, rs * (grad_n(gv, wsc) - h * cc), rv);
+            split_store_scalar<T, CPT>(dx, in.at.e0, c, rs * (grad_n(gv, wsc) - h * cc), rv);
         }
-    }
+    };
+    tile_loop<PF, In>(c, fetch, body);
     if constexpr (PG) split_write_partials<T, CPT, 1>(ws + c.wg * g.ws_rs, g.ws_cs, acc, accs, c, g, part);
 }
 

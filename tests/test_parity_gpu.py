@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import row_wise_normalization_dyt_amd as rwn
+from row_wise_normalization_dyt_amd import autograd as ag
 import workloads
 from tests import gpu_cases as gc
 from tests import tolerance as tol
@@ -270,6 +271,65 @@ def test_dx_only_backward_matches_full_backward(layer):
         torch.cuda.synchronize()
         assert all(t is None for t in only[1:])
         assert torch.equal(only[0].view(torch.uint8), full[0].view(torch.uint8)), wl.name
+
+
+LN_GRAD_SHAPES = [(4099, 24, "f32", "f32"), (1031, 128, "bf16", "f32"), (263, 1024, "bf16", "bf16"),
+                  (257, 1025, "bf16", "f32"), (65, 17, "f16", "f16"), (67, 4096, "f32", "f32"),
+                  (129, 3001, "f16", "f32"), (401408, 24, "f32", "f32")]
+
+
+@pytest.mark.parametrize("which", ["dgamma", "dbeta"])
+def test_layernorm_single_gradient_matches_full_backward(which):
+    """One LayerNorm parameter gradient alone (flat, general, split, scalar and wide shapes, and
+    the 401408 x 24 float32 size): dx and that gradient are bitwise the full backward's, the
+    other is not returned, and stage 1 writes half the partial slots of a NaN-poisoned
+    workspace (only the requested gradient's columns)."""
+    for (M, N, xdt, pdt) in LN_GRAD_SHAPES:
+        wl = workloads.small("layernorm", M, N, xdt, pdt, seed=M + 3 * N)
+        _banner(wl, which, "only")
+        inp = {k: v.to(DEV) for k, v in workloads.make_inputs(wl, DEV).items()}
+        x, dy, g = inp["x"], inp["dy"], inp["gamma"]
+        _, mean, rstd = rwn.layernorm_fwd(x, g, inp["beta"], wl.eps)
+        ws_full, ws_one = gc._poisoned_ws("layernorm", x), gc._poisoned_ws("layernorm", x)
+        full = rwn.layernorm_bwd(x, dy, mean, rstd, g, wl.eps, workspace=ws_full)
+        one = rwn.layernorm_bwd(x, dy, mean, rstd, g, wl.eps, need_dgamma=which == "dgamma",
+                                need_dbeta=which == "dbeta", workspace=ws_one)
+        torch.cuda.synchronize()
+        k = 1 if which == "dgamma" else 2
+        assert one[3 - k] is None, wl.name
+        assert torch.equal(one[0].view(torch.uint8), full[0].view(torch.uint8)), wl.name
+        assert torch.equal(one[k].view(torch.uint8), full[k].view(torch.uint8)), wl.name
+        n = ws_full.numel() // 4 * 4
+        written_full = int(torch.isfinite(ws_full[:n].view(torch.float32)).sum())
+        written_one = int(torch.isfinite(ws_one[:n].view(torch.float32)).sum())
+        assert written_one * 2 == written_full, (wl.name, written_one, written_full)
+
+
+@pytest.mark.parametrize("trainable", ["weight", "bias"])
+def test_layernorm_autograd_one_trainable_parameter(trainable):
+    """nn.LayerNorm-style use with one parameter frozen, and with gamma but no bias: the autograd
+    function asks only for the trainable parameter's gradient; y, dx and that gradient match
+    the oracle (a missing bias is zero, its gradient is not formed)."""
+    for (M, N, xdt, pdt), no_bias in [((1001, 24, "f32", "f32"), False), ((257, 1025, "bf16", "f32"), False),
+                                      ((999, 48, "f32", "f32"), True), ((131, 4096, "bf16", "bf16"), True)]:
+        if no_bias and trainable == "bias":
+            continue
+        wl = workloads.small("layernorm", M, N, xdt, pdt, seed=M + N)
+        _banner(wl, "trainable", trainable, "no bias" if no_bias else "")
+        inp = workloads.make_inputs(wl)
+        if no_bias:
+            inp["beta"] = torch.zeros_like(inp["beta"])
+        x = inp["x"].to(DEV).requires_grad_(True)
+        w = inp["gamma"].to(DEV).requires_grad_(trainable == "weight")
+        b = None if no_bias else inp["beta"].to(DEV).requires_grad_(trainable == "bias")
+        y = ag.layer_norm(x, w, b, wl.eps)
+        y.backward(inp["dy"].to(DEV))
+        torch.cuda.synchronize()
+        assert (w.grad is None) == (trainable != "weight")
+        assert b is None or (b.grad is None) == (trainable != "bias")
+        gpu = {"y": y.detach(), "dx": x.grad, "dgamma": w.grad, "dbeta": None if b is None else b.grad}
+        ora = gc.oracle_run("layernorm", inp, wl.eps)
+        tol.assert_reports(gc.compare("layernorm", gpu, ora, gc.DT[xdt], gc.DT[pdt]))
 
 
 # Workloads compared on every element of y, dx and the statistics (the oracle streams row
