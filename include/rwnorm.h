@@ -17,7 +17,7 @@
  *            element-aligned address is accepted, but x, dy, y and dx of one call must share
  *            the same address modulo 16 bytes (fresh allocations always do).  Parameters are
  *            contiguous [N] vectors; alpha is a one-element device buffer; statistics are
- *            float32 [M].
+ *            float32 [M].  The *_strided entry points take strided rows and parameters.
  * Dtypes     x, dy, y, dx use x_dtype.  The parameters (alpha, gamma, beta, weight) and their
  *            gradients use param_dtype.  Supported pairs (x_dtype, param_dtype): (F32, F32),
  *            (BF16, F32), (BF16, BF16), (F16, F32), (F16, F16).  Arithmetic is float32;
@@ -177,6 +177,69 @@ rwn_status rmsnorm_bwd_form(int64_t M, int64_t N, const void* x, const void* dy,
                             rwn_rms_form form, void* dx, void* dweight, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------- strided operands */
+
+/* The six entry points above with strided row operands and parameter vectors, so that views
+ * (a slice of a wider matrix, a head-major [B, S, H, D] tensor whose rows are D-wide, a
+ * gradient in another layout than x) run without copies.  The DeepSpeed RMSNorm pages
+ * (PR #8645, "Where the kernels run" and "Correctness evidence"; PR #8664, Tests) test
+ * head-major non-contiguous inputs, transposed incoming gradients and non-contiguous weights.
+ *
+ * Rows     The M rows are the index space of nlead (1..3) leading dimensions of sizes
+ *          lead[0..nlead-1] (host array; M = their product, at most 2^31 - 1), the last one
+ *          fastest.  Each row operand has its own host array of nlead element strides:
+ *          row (i_0, ..., i_{nlead-1}) starts at sum_k i_k * strides[k] elements past the
+ *          operand's base, and its N elements are contiguous.  Statistics (mean, rstd) are
+ *          contiguous float32 [M] in that row order.  Strides must be >= 0; an output (y, dx)
+ *          whose rows would share an element returns RWN_ERR_INVALID_ARG; an operand spanning
+ *          more than 2^31 - 32 bytes returns RWN_ERR_UNSUPPORTED.
+ * Params   gamma_stride / beta_stride / weight_stride: element strides (>= 0) of the parameter
+ *          vectors.  alpha is one element.  Parameter gradients are written contiguous.
+ * Kernels  Operands that are dense [M, N] after all, at one address modulo 16, with contiguous
+ *          parameters, take exactly the dense entry points' path.  Otherwise, when every row of
+ *          every operand starts at one offset modulo 16 bytes (bases at one address modulo 16,
+ *          strides multiples of 16 bytes), rows move in 16-byte chunks as in the dense path
+ *          (LayerNorm / RMSNorm rows not a whole number of aligned chunks take N <= 16384 - V + 1,
+ *          V the elements of a chunk); else element by element, which takes N <= 2048 (16-bit)
+ *          or 4096 (float32) for LayerNorm / RMSNorm and any N for DyT.  Either way results follow the same
+ *          arithmetic as the dense entry points; the backward's workspace is sized by the
+ *          *_bwd_workspace_size queries, which cover strided plans.
+ * All other arguments, rules and errors are those of the dense entry point of the same name. */
+rwn_status dyt_fwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                           const int64_t* x_strides, rwn_dtype x_dtype, const void* alpha,
+                           const void* gamma, int64_t gamma_stride, const void* beta,
+                           int64_t beta_stride, rwn_dtype param_dtype, void* y,
+                           const int64_t* y_strides, void* stream);
+rwn_status dyt_bwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                           const int64_t* x_strides, const void* dy, const int64_t* dy_strides,
+                           rwn_dtype x_dtype, const void* alpha, const void* gamma,
+                           int64_t gamma_stride, rwn_dtype param_dtype, void* dx,
+                           const int64_t* dx_strides, void* dalpha, void* dgamma, void* dbeta,
+                           void* workspace, size_t workspace_bytes, void* stream);
+rwn_status layernorm_fwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                                 const int64_t* x_strides, rwn_dtype x_dtype, const void* gamma,
+                                 int64_t gamma_stride, const void* beta, int64_t beta_stride,
+                                 rwn_dtype param_dtype, float eps, void* y, const int64_t* y_strides,
+                                 float* mean, float* rstd, void* stream);
+rwn_status layernorm_bwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                                 const int64_t* x_strides, const void* dy, const int64_t* dy_strides,
+                                 rwn_dtype x_dtype, const float* mean, const float* rstd,
+                                 const void* gamma, int64_t gamma_stride, rwn_dtype param_dtype,
+                                 float eps, void* dx, const int64_t* dx_strides, void* dgamma,
+                                 void* dbeta, void* workspace, size_t workspace_bytes, void* stream);
+rwn_status rmsnorm_fwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                               const int64_t* x_strides, rwn_dtype x_dtype, const void* weight,
+                               int64_t weight_stride, rwn_dtype weight_dtype, float eps,
+                               rwn_rms_form form, void* y, const int64_t* y_strides, float* rstd,
+                               void* stream);
+rwn_status rmsnorm_bwd_strided(int nlead, const int64_t* lead, int64_t N, const void* x,
+                               const int64_t* x_strides, const void* dy, const int64_t* dy_strides,
+                               rwn_dtype x_dtype, const float* rstd, const void* weight,
+                               int64_t weight_stride, rwn_dtype weight_dtype, float eps,
+                               rwn_rms_form form, void* dx, const int64_t* dx_strides,
+                               void* dweight, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* ------------------------------------------------------------------------------ support */
 
 /* Message of the last failed call on this thread ("" after a successful call). */
@@ -222,9 +285,11 @@ rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t
  * workspace is).  misalign_bytes is the common address of x/y/dy/dx modulo 16.  cus: 0 plans
  * for the current device exactly as the entry points do (its CU count, and the workgroups of
  * the chosen kernel that fit on one CU at once); any other value plans for that many CUs from
- * launch bounds alone, without touching a device. */
+ * launch bounds alone, without touching a device.  layout: 0 for dense operands, 1 for strided
+ * operands whose rows all start misalign_bytes past a 16-byte boundary, 2 for strided operands
+ * of mixed alignment (the *_strided entry points choose it). */
 rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_dtype x_dtype,
-                    int param_dtype, int misalign_bytes, int cus, int64_t* out);
+                    int param_dtype, int misalign_bytes, int cus, int layout, int64_t* out);
 
 #ifdef __cplusplus
 }

@@ -1,9 +1,10 @@
 """Row-wise normalization for MI355X (gfx950): DyT, LayerNorm and RMSNorm, forward and backward.
 
 Thin binding over librwnorm's C ABI (include/rwnorm.h), with the same entry-point names.  It
-only marshals arguments: shapes and dtypes are checked, leading dimensions flattened to [M, N],
-non-contiguous inputs copied, outputs and the backward workspace allocated with torch, and the
-call enqueued on the current stream of the tensors' device.  Every step of the computation
+only marshals arguments: shapes and dtypes are checked, contiguous inputs flattened to [M, N],
+non-contiguous ones handed to the strided entry points with their strides, outputs and the
+backward workspace allocated with torch, and the call enqueued on the current stream of the
+tensors' device.  Every step of the computation
 runs in the library's HIP kernels; there is no other implementation to fall back to.
 """
 from __future__ import annotations
@@ -131,6 +132,96 @@ def _out_rows(given: Optional[torch.Tensor], x2: torch.Tensor, name: str) -> tor
     return given.view(x2.shape)
 
 
+# ------------------------------------------------------------------------- strided operands
+#
+# A non-contiguous x or dy (a slice of a wider matrix, a head-major view, a transposed incoming
+# gradient) or a non-contiguous parameter vector goes to the *_strided entry points as it is:
+# the leading dimensions are handed over with each tensor's own strides (size-1 dimensions
+# dropped, neighbours merged where every tensor allows), and nothing is copied.  Only a last
+# dimension that is not contiguous, more than three leading dimensions that do not merge, or
+# a shape the strided kernels do not take (rows of different alignment wider than the
+# element-wise kernels' limit) fall back to contiguous copies.  Fresh outputs are contiguous.
+
+def _rows_view(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have at least one dimension")
+    return t if (t.shape[-1] == 1 or t.stride(-1) == 1) else t.contiguous()
+
+
+def _use_strided(rows, params) -> bool:
+    if any(not t.is_cuda or t.dim() < 1 or t.numel() == 0 for t in rows):
+        return False
+    if any(t.shape[-1] > 1 and t.stride(-1) != 1 for t in rows):
+        return False
+    return any(not t.is_contiguous() for t in rows) or \
+        any(p is not None and p.numel() > 1 and not p.is_contiguous() for p in params)
+
+
+def _fresh_rows(x: torch.Tensor) -> torch.Tensor:
+    """A contiguous tensor of x's shape and dtype at x's address modulo 16 bytes."""
+    esz = x.element_size()
+    if x.data_ptr() % 16 == 0:
+        return torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    buf = torch.empty(x.numel() + 16 // esz, dtype=x.dtype, device=x.device)
+    shift = ((x.data_ptr() - buf.data_ptr()) % 16) // esz
+    return buf[shift:shift + x.numel()].view(x.shape)
+
+
+def _out_strided(given: Optional[torch.Tensor], x: torch.Tensor, name: str) -> torch.Tensor:
+    if given is None:
+        return _fresh_rows(x)
+    if given.device != x.device or given.dtype != x.dtype or given.shape != x.shape:
+        raise ValueError(f"{name} must be a {x.dtype} tensor of shape {tuple(x.shape)} on {x.device}")
+    if x.shape[-1] > 1 and given.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return given
+
+
+def _svec(p: Optional[torch.Tensor], n: int, name: str, dev):
+    """(1-D view of a parameter vector, its element stride); no copy where a view exists."""
+    if p is None:
+        return None, 1
+    if p.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if p.numel() != n:
+        raise ValueError(f"{name} must have {n} elements (got {p.numel()})")
+    v = p.reshape(-1)
+    return v, (v.stride(0) if n > 1 else 1)
+
+
+def _row_layout(ts):
+    """(nlead, lead sizes, [strides of each tensor]) as ctypes arrays for tensors of one shape
+    [..., N], or None when more than three leading dimensions remain after merging."""
+    dims = []
+    for i, size in enumerate(ts[0].shape[:-1]):
+        if size == 1:
+            continue
+        st = [t.stride(i) for t in ts]
+        if dims and all(ps == s * size for ps, s in zip(dims[-1][1], st)):
+            dims[-1] = (dims[-1][0] * size, st)
+        else:
+            dims.append((size, st))
+    if not dims:
+        dims = [(1, [0] * len(ts))]
+    if len(dims) > 3:
+        return None
+    n = len(dims)
+    lead = (ctypes.c_int64 * n)(*[d[0] for d in dims])
+    strides = [(ctypes.c_int64 * n)(*[d[1][k] for d in dims]) for k in range(len(ts))]
+    return n, lead, strides
+
+
+def _try_strided(lib, fn: str, call) -> bool:
+    """Runs call(); False (nothing launched) when the strided kernels do not take the shape."""
+    code = call()
+    if code == 2:   # RWN_ERR_UNSUPPORTED: validated before any launch
+        return False
+    _lib.check(lib, fn, code)
+    return True
+
+
 def _out_vec(given: Optional[torch.Tensor], n: int, dtype, dev, name: str) -> torch.Tensor:
     """A length-n output vector: fresh, or the caller's contiguous buffer of that dtype."""
     if given is None:
@@ -147,6 +238,20 @@ def dyt_fwd(x: torch.Tensor, alpha: torch.Tensor, gamma: torch.Tensor, beta: tor
     """y = gamma * tanh(alpha * x) + beta over the last dimension; y has x's shape and dtype.
     y=: an output buffer to write instead of a fresh tensor."""
     lib = _L()
+    if _use_strided([x], [gamma, beta]):
+        xs = _rows_view(x, "x")
+        N = xs.shape[-1]
+        a = _vec(alpha, 1, "alpha", xs.device)
+        (g, gs), (b, bs) = _svec(gamma, N, "gamma", xs.device), _svec(beta, N, "beta", xs.device)
+        ys = _out_strided(y, xs, "y")
+        lay = _row_layout([xs, ys])
+        if lay is not None:
+            n, lead, (sx, sy) = lay
+            with torch.cuda.device(xs.device):
+                if _try_strided(lib, "dyt_fwd_strided", lambda: lib.dyt_fwd_strided(
+                        n, lead, N, _ptr(xs), sx, _dt(xs, "x"), _ptr(a), _ptr(g), gs, _ptr(b), bs,
+                        _param_dtype(a, g, b), _ptr(ys), sy, _stream(xs.device))):
+                    return ys
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     alpha, gamma, beta = _vec(alpha, 1, "alpha", x2.device), _vec(gamma, N, "gamma", x2.device), _vec(beta, N, "beta", x2.device)
@@ -164,9 +269,29 @@ def dyt_bwd(x: torch.Tensor, dy: torch.Tensor, alpha: torch.Tensor, gamma: torch
     """Returns (dx, dalpha [1], dgamma [N], dbeta [N]); gradients in the parameters' dtype.
     dx=, dalpha=, dgamma=, dbeta=, workspace=: buffers to use instead of fresh tensors."""
     lib = _L()
-    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
-    if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
+    if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
+    if _use_strided([x, dy], [gamma]):
+        xs, dys = _rows_view(x, "x"), _rows_view(dy, "dy")
+        N = xs.shape[-1]
+        a = _vec(alpha, 1, "alpha", xs.device)
+        g, gs = _svec(gamma, N, "gamma", xs.device)
+        dxs = _out_strided(dx, xs, "dx")
+        lay = _row_layout([xs, dys, dxs])
+        if lay is not None:
+            n, lead, (sx, sdy, sdx) = lay
+            M = xs.numel() // N
+            da = _out_vec(dalpha, 1, g.dtype, xs.device, "dalpha") if need_param_grads else None
+            dg = _out_vec(dgamma, N, g.dtype, xs.device, "dgamma") if need_param_grads else None
+            db = _out_vec(dbeta, N, g.dtype, xs.device, "dbeta") if need_param_grads else None
+            with torch.cuda.device(xs.device):
+                ws = _workspace("dyt", M, N, xs.dtype, xs.device, workspace) if need_param_grads else None
+                if _try_strided(lib, "dyt_bwd_strided", lambda: lib.dyt_bwd_strided(
+                        n, lead, N, _ptr(xs), sx, _ptr(dys), sdy, _dt(xs, "x"), _ptr(a), _ptr(g), gs,
+                        _param_dtype(a, g), _ptr(dxs), sdx, _ptr(da), _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),
+                        _stream(xs.device))):
+                    return dxs, da, dg, db
+    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     x2, dy2 = _pair(x2, dy2)
     M, N = x2.shape
     alpha, gamma = _vec(alpha, 1, "alpha", x2.device), _vec(gamma, N, "gamma", x2.device)
@@ -191,6 +316,23 @@ def layernorm_fwd(x: torch.Tensor, gamma: Optional[torch.Tensor], beta: Optional
     """Returns (y, mean [M] float32, rstd [M] float32); mean/rstd are None if not wanted.
     y=, mean=, rstd=: buffers to write instead of fresh tensors."""
     lib = _L()
+    if _use_strided([x], [gamma, beta]):
+        xs = _rows_view(x, "x")
+        N = xs.shape[-1]
+        M = xs.numel() // N
+        (g, gs), (b, bs) = _svec(gamma, N, "gamma", xs.device), _svec(beta, N, "beta", xs.device)
+        pd = _param_dtype(g, b) if (g is not None or b is not None) else _lib.RWN_F32
+        ys = _out_strided(y, xs, "y")
+        lay = _row_layout([xs, ys])
+        if lay is not None:
+            n, lead, (sx, sy) = lay
+            mu = _out_vec(mean, M, torch.float32, xs.device, "mean") if want_stats else None
+            rs = _out_vec(rstd, M, torch.float32, xs.device, "rstd") if want_stats else None
+            with torch.cuda.device(xs.device):
+                if _try_strided(lib, "layernorm_fwd_strided", lambda: lib.layernorm_fwd_strided(
+                        n, lead, N, _ptr(xs), sx, _dt(xs, "x"), _ptr(g), gs, _ptr(b), bs, pd, float(eps), _ptr(ys),
+                        sy, _ptr(mu), _ptr(rs), _stream(xs.device))):
+                    return ys, mu, rs
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     gamma, beta = _vec(gamma, N, "gamma", x2.device), _vec(beta, N, "beta", x2.device)
@@ -216,21 +358,42 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
     not wanted is returned as None and its column partials are never formed.
     dx=, dgamma=, dbeta=, workspace=: buffers to use instead of fresh tensors."""
     lib = _L()
-    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
-    if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
+    if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
+    want_g = need_param_grads if need_dgamma is None else need_dgamma
+    want_b = need_param_grads if need_dbeta is None else need_dbeta
+    for t, nm in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    if _use_strided([x, dy], [gamma]):
+        xs, dys = _rows_view(x, "x"), _rows_view(dy, "dy")
+        N = xs.shape[-1]
+        M = xs.numel() // N
+        g, gs = _svec(gamma, N, "gamma", xs.device)
+        pdtype = g.dtype if g is not None else (param_dtype or torch.float32)
+        dxs = _out_strided(dx, xs, "dx")
+        lay = _row_layout([xs, dys, dxs])
+        if lay is not None:
+            n, lead, (sx, sdy, sdx) = lay
+            mu = _vec(mean, M, "mean", xs.device) if mean is not None else None
+            rs = _vec(rstd, M, "rstd", xs.device) if rstd is not None else None
+            dg = _out_vec(dgamma, N, pdtype, xs.device, "dgamma") if want_g else None
+            db = _out_vec(dbeta, N, pdtype, xs.device, "dbeta") if want_b else None
+            with torch.cuda.device(xs.device):
+                ws = _workspace("layernorm", M, N, xs.dtype, xs.device, workspace) if (want_g or want_b) else None
+                if _try_strided(lib, "layernorm_bwd_strided", lambda: lib.layernorm_bwd_strided(
+                        n, lead, N, _ptr(xs), sx, _ptr(dys), sdy, _dt(xs, "x"), _ptr(mu), _ptr(rs), _ptr(g), gs,
+                        _DT[pdtype], float(eps), _ptr(dxs), sdx, _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),
+                        _stream(xs.device))):
+                    return dxs, dg, db
+    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     x2, dy2 = _pair(x2, dy2)
     M, N = x2.shape
     gamma = _vec(gamma, N, "gamma", x2.device)
     pdtype = gamma.dtype if gamma is not None else (param_dtype or torch.float32)
     mean = _vec(mean, M, "mean", x2.device) if mean is not None else None
     rstd = _vec(rstd, M, "rstd", x2.device) if rstd is not None else None
-    for t, nm in ((mean, "mean"), (rstd, "rstd")):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{nm} must be float32")
     dx = _out_rows(dx, x2, "dx")
-    want_g = need_param_grads if need_dgamma is None else need_dgamma
-    want_b = need_param_grads if need_dbeta is None else need_dbeta
     dg = _out_vec(dgamma, N, pdtype, x2.device, "dgamma") if want_g else None
     db = _out_vec(dbeta, N, pdtype, x2.device, "dbeta") if want_b else None
     with torch.cuda.device(x2.device):
@@ -259,6 +422,21 @@ def rmsnorm_fwd(x: torch.Tensor, weight: torch.Tensor, eps: float, want_stats: b
     """Returns (y, rstd [M] float32 or None); y keeps x's dtype.  form: "cast_then_weight"
     (Llama), "weight_then_cast" or "one_plus_weight" (Gemma).  y=, rstd=: buffers to write."""
     lib = _L()
+    if _use_strided([x], [weight]):
+        xs = _rows_view(x, "x")
+        N = xs.shape[-1]
+        M = xs.numel() // N
+        w, ws_ = _svec(weight, N, "weight", xs.device)
+        ys = _out_strided(y, xs, "y")
+        lay = _row_layout([xs, ys])
+        if lay is not None:
+            n, lead, (sx, sy) = lay
+            rs = _out_vec(rstd, M, torch.float32, xs.device, "rstd") if want_stats else None
+            with torch.cuda.device(xs.device):
+                if _try_strided(lib, "rmsnorm_fwd_strided", lambda: lib.rmsnorm_fwd_strided(
+                        n, lead, N, _ptr(xs), sx, _dt(xs, "x"), _ptr(w), ws_, _dt(w, "weight"), float(eps),
+                        _form(form), _ptr(ys), sy, _ptr(rs), _stream(xs.device))):
+                    return ys, rs
     x2 = _as_2d(x, "x")
     M, N = x2.shape
     weight = _vec(weight, N, "weight", x2.device)
@@ -278,15 +456,33 @@ def rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, rstd: Optional[torch.Tensor],
     """Returns (dx, dweight).  rstd None: recomputed from x.  dx=, dweight=, workspace=: buffers
     to use instead of fresh tensors."""
     lib = _L()
-    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
-    if dy2.shape != x2.shape or dy2.dtype != x2.dtype:
+    if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
+    if rstd is not None and rstd.dtype != torch.float32:
+        raise TypeError("rstd must be float32")
+    if _use_strided([x, dy], [weight]):
+        xs, dys = _rows_view(x, "x"), _rows_view(dy, "dy")
+        N = xs.shape[-1]
+        M = xs.numel() // N
+        w, ws_ = _svec(weight, N, "weight", xs.device)
+        dxs = _out_strided(dx, xs, "dx")
+        lay = _row_layout([xs, dys, dxs])
+        if lay is not None:
+            n, lead, (sx, sdy, sdx) = lay
+            rs = _vec(rstd, M, "rstd", xs.device) if rstd is not None else None
+            dw = _out_vec(dweight, N, w.dtype, xs.device, "dweight") if need_param_grads else None
+            with torch.cuda.device(xs.device):
+                wsp = _workspace("rmsnorm", M, N, xs.dtype, xs.device, workspace) if need_param_grads else None
+                if _try_strided(lib, "rmsnorm_bwd_strided", lambda: lib.rmsnorm_bwd_strided(
+                        n, lead, N, _ptr(xs), sx, _ptr(dys), sdy, _dt(xs, "x"), _ptr(rs), _ptr(w), ws_,
+                        _dt(w, "weight"), float(eps), _form(form), _ptr(dxs), sdx, _ptr(dw), _ptr(wsp),
+                        _ws_bytes(wsp), _stream(xs.device))):
+                    return dxs, dw
+    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
     x2, dy2 = _pair(x2, dy2)
     M, N = x2.shape
     weight = _vec(weight, N, "weight", x2.device)
     rstd = _vec(rstd, M, "rstd", x2.device) if rstd is not None else None
-    if rstd is not None and rstd.dtype != torch.float32:
-        raise TypeError("rstd must be float32")
     dx = _out_rows(dx, x2, "dx")
     dw = _out_vec(dweight, N, weight.dtype, x2.device, "dweight") if need_param_grads else None
     with torch.cuda.device(x2.device):
@@ -337,14 +533,15 @@ def stream_probe(src: torch.Tensor, dst: torch.Tensor, src2: Optional[torch.Tens
 
 
 def plan(layer: str, backward: bool, M: int, N: int, dtype: torch.dtype, misalign_bytes: int = 0,
-         cus: int = 0, param_dtype: Optional[torch.dtype] = None):
+         cus: int = 0, param_dtype: Optional[torch.dtype] = None, layout: int = 0):
     """The launch plan the library picks.  cus = 0 plans for the current device, as the entry
     points do; any other value plans for that many compute units without touching a device."""
     lib = _L()
     out = (ctypes.c_int64 * 16)()
     li = {"dyt": 0, "layernorm": 1, "rmsnorm": 2}[layer]
     pd = -1 if param_dtype is None else _DT[param_dtype]
-    _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], pd, misalign_bytes, cus, out))
+    _lib.check(lib, "rwn_plan", lib.rwn_plan(li, int(backward), M, N, _DT[dtype], pd, misalign_bytes, cus,
+                                             int(layout), out))
     keys = ("mode", "cpt", "rt", "tpr", "rpp", "block", "grid", "ntiles", "vec", "kt", "strided", "ncb", "xcd_remap",
             "prefetch", "flat", "split")
     return dict(zip(keys, [int(v) for v in out]))

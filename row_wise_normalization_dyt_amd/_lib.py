@@ -23,6 +23,7 @@ KERNEL_TAGS = {1: "dyt_fwd", 2: "dyt_bwd", 3: "layernorm_fwd", 4: "layernorm_bwd
 
 _i64, _vp, _ci, _cf, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _fp = ctypes.c_void_p   # float* (device)
+_ip = ctypes.POINTER(ctypes.c_int64)   # const int64_t* (host array)
 
 SIGNATURES = {
     "dyt_fwd": (_ci, [_i64, _i64, _vp, _ci, _vp, _vp, _vp, _ci, _vp, _vp]),
@@ -37,12 +38,22 @@ SIGNATURES = {
     "rmsnorm_bwd_workspace_size": (_ci, [_i64, _i64, _ci, ctypes.POINTER(_sz)]),
     "rmsnorm_fwd_form": (_ci, [_i64, _i64, _vp, _ci, _vp, _ci, _cf, _ci, _vp, _fp, _vp]),
     "rmsnorm_bwd_form": (_ci, [_i64, _i64, _vp, _vp, _ci, _fp, _vp, _ci, _cf, _ci, _vp, _vp, _vp, _sz, _vp]),
+    "dyt_fwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _ci, _vp, _vp, _i64, _vp, _i64, _ci, _vp, _ip, _vp]),
+    "dyt_bwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _vp, _ip, _ci, _vp, _vp, _i64, _ci, _vp, _ip, _vp, _vp, _vp,
+                              _vp, _sz, _vp]),
+    "layernorm_fwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _ci, _vp, _i64, _vp, _i64, _ci, _cf, _vp, _ip, _fp, _fp,
+                                    _vp]),
+    "layernorm_bwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _vp, _ip, _ci, _fp, _fp, _vp, _i64, _ci, _cf, _vp, _ip,
+                                    _vp, _vp, _vp, _sz, _vp]),
+    "rmsnorm_fwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _ci, _vp, _i64, _ci, _cf, _ci, _vp, _ip, _fp, _vp]),
+    "rmsnorm_bwd_strided": (_ci, [_ci, _ip, _i64, _vp, _ip, _vp, _ip, _ci, _fp, _vp, _i64, _ci, _cf, _ci, _vp, _ip,
+                                  _vp, _vp, _sz, _vp]),
     "rwn_last_error": (ctypes.c_char_p, []),
     "rwn_version": (ctypes.c_char_p, []),
     "rwn_trace_begin": (_ci, [_ci]),
     "rwn_trace_end": (_ci, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int), _ci]),
     "rwn_stream_probe": (_ci, [_vp, _vp, _vp, _sz, _ci, _ci, _ci, _vp]),
-    "rwn_plan": (_ci, [_ci, _ci, _i64, _i64, _ci, _ci, _ci, _ci, ctypes.POINTER(_i64)]),
+    "rwn_plan": (_ci, [_ci, _ci, _i64, _i64, _ci, _ci, _ci, _ci, _ci, ctypes.POINTER(_i64)]),
 }
 
 

@@ -205,7 +205,7 @@ static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pd
 }
 
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
-               int cus, bool occupancy, Plan* out) {
+               int cus, bool occupancy, Plan* out, int layout) {
     static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
     static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 0);
     static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
@@ -221,11 +221,15 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     Plan p;
     p.M = M;
     p.N = N;
+    p.layout = layout;
     const int esz = xdt == DT_F32 ? 4 : 2;
     const int V = 16 / esz;
     const int b = misalign_bytes / esz;
     int64_t chunks;
-    if (N % V == 0 && b == 0) {
+    if (layout == 2) {
+        p.mode = MODE_SCALAR;
+        chunks = N;
+    } else if (N % V == 0 && b == 0) {
         p.mode = MODE_ALIGNED;
         chunks = N / V;
     } else {
@@ -251,7 +255,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     if (p.mode == MODE_SHIFTED) split_max_w = 8;
     else if (p.mode == MODE_ALIGNED && chunks > 64)
         split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT) ? 4 : 2;
-    if (split_max_w && split_rows && prefetch < 0 &&
+    if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
         plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, xcd_remap,
                    split_max_w, &p)) {
         *out = p;
@@ -271,9 +275,10 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.tpr = (int)chunks;
         p.cpt = 1;
         packed = true;
-    } else if (layer == LAYER_DYT && chunks > 64 && p.mode != MODE_SCALAR) {
+    } else if (layer == LAYER_DYT && chunks > 64 && (p.mode != MODE_SCALAR || layout == 2)) {
         // DyT has no row reduction: wide rows are cut into ncb column blocks of W <= 8 waves,
-        // one chunk per lane (its per-element state is the largest of the three layers).
+        // one chunk per lane (its per-element state is the largest of the three layers); so are
+        // strided rows of any alignment, one element per lane.
         // Fewest idle lanes, ties to the widest block.
         int64_t best = -1;
         for (int w = 8; w >= 1; --w) {
@@ -336,6 +341,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     const int bwd_rt_auto = (layer == LAYER_DYT && p.tpr >= 32) ? 2 : 1;
     p.rt = narrow_aligned ? (backward ? (bwd_rt > 0 ? bwd_rt : bwd_rt_auto) : fwd_rt) : 1;
     if (p.rt == 3) p.rt = 2;
+    if (layout) p.rt = 1;
 
     // Row slots: narrow rows fill 256-thread workgroups; wide rows use wide_block threads.
     // SHIFTED slots each carry their own shift, so a strided SHIFTED workgroup has one slot,
@@ -344,7 +350,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // A blocked SHIFTED workgroup walks consecutive tiles, so its slots must be V rows apart
     // (rpp = V) for each slot to keep one shift; where V slots do not fit in a workgroup the
     // backward stays strided.
-    bool blocked = backward && blocked_k > 0 && p.ncb == 1;
+    bool blocked = backward && blocked_k > 0 && p.ncb == 1 && layout == 0;
     if (p.mode == MODE_SHIFTED) {
         if (blocked && (int64_t)p.tpr * V <= max_block(p.rt, p.cpt, esz)) {
             p.rpp = V;
@@ -378,10 +384,11 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             p.pf = 1;
         else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
     }
+    if (layout) p.pf = 0;
     // Narrow aligned LayerNorm rows, one chunk and one row per thread, take the flat kernels
     // (plain loads on clamped row indices, no per-tile descriptors), which run fastest without
     // pipelining.
-    if (flat_rows && prefetch < 0 && layer == LAYER_LN && p.mode == MODE_ALIGNED && p.cpt == 1 &&
+    if (flat_rows && prefetch < 0 && layout == 0 && layer == LAYER_LN && p.mode == MODE_ALIGNED && p.cpt == 1 &&
         p.rt == 1 && p.tpr <= 64 && p.ncb == 1) {
         p.flat = 1;
         p.pf = 0;

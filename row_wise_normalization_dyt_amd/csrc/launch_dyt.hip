@@ -13,12 +13,12 @@ hipError_t launch_dyt_fwd(const Plan& p, int xdt, int pdt, const void* x, const 
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
             else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             else return launch(dyt_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                               decltype(rt)::value, decltype(pf)::value>,
+                                               decltype(rt)::value, decltype(pf)::value, decltype(lay)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)alpha, (const PT*)gamma, (const PT*)beta, (T*)y, g);
         });
@@ -34,12 +34,12 @@ hipError_t launch_dyt_bwd(const Plan& p, int xdt, int pdt, const void* x, const 
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
-            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
                 constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
                 if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
                 else if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
                 else return launch(dyt_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                                  decltype(rt)::value, decltype(pf)::value, decltype(pg)::value>,
+                                                  decltype(rt)::value, decltype(pf)::value, decltype(pg)::value, decltype(lay)::value>,
                                    dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                                    (const T*)dy, (const PT*)alpha, (const PT*)gamma, (T*)dx, ws, g);
             });
@@ -53,13 +53,13 @@ int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt) {
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
             if constexpr (decltype(cpt)::value > 1) return hipErrorInvalidValue;
             else {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
-                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
-                const void* k = backward ? (const void*)dyt_bwd_kernel<T, PT, M_, C_, R_, P_, 1>
-                                         : (const void*)dyt_fwd_kernel<T, PT, M_, C_, R_, P_>;
+                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value, L_ = decltype(lay)::value;
+                const void* k = backward ? (const void*)dyt_bwd_kernel<T, PT, M_, C_, R_, P_, 1, L_>
+                                         : (const void*)dyt_fwd_kernel<T, PT, M_, C_, R_, P_, L_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;
             }

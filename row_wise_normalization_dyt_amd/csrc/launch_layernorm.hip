@@ -14,11 +14,11 @@ hipError_t launch_ln_fwd(const Plan& p, int xdt, int pdt, const void* x, const v
     return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
             constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
             if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
             return launch(ln_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                              decltype(rt)::value, decltype(pf)::value>,
+                                              decltype(rt)::value, decltype(pf)::value, decltype(lay)::value>,
                                dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                                (const PT*)gamma, (const PT*)beta, eps, (T*)y, mean, rstd, g);
         });
@@ -35,11 +35,11 @@ hipError_t launch_ln_bwd(const Plan& p, int xdt, int pdt, const void* x, const v
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
-            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
                 constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
                 if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
                 return launch(ln_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                            decltype(rt)::value, decltype(pf)::value, decltype(pg)::value>,
+                                            decltype(rt)::value, decltype(pf)::value, decltype(pg)::value, decltype(lay)::value>,
                               dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                               (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
             });
@@ -54,12 +54,12 @@ int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt) {
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
             {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
-                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
-                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_, 3>
-                                         : (const void*)ln_fwd_kernel<T, PT, M_, C_, R_, P_>;
+                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value, L_ = decltype(lay)::value;
+                const void* k = backward ? (const void*)ln_bwd_kernel<T, PT, M_, C_, R_, P_, 3, L_>
+                                         : (const void*)ln_fwd_kernel<T, PT, M_, C_, R_, P_, L_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;
             }

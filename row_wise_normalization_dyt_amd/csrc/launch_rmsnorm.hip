@@ -23,11 +23,11 @@ hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const vo
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
-            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+            return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
                 constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
                 if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
                 return launch(rms_fwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
-                                             decltype(rt)::value, decltype(pf)::value, decltype(var)::value>,
+                                             decltype(rt)::value, decltype(pf)::value, decltype(var)::value, decltype(lay)::value>,
                               dim3((unsigned)p.grid), dim3(p.block), 0, s, (const T*)x,
                               (const PT*)w, eps, (T*)y, rstd, g);
             });
@@ -45,12 +45,12 @@ hipError_t launch_rms_bwd(const Plan& p, int xdt, int pdt, int variant, const vo
             return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
                 using T = typename decltype(tt)::type;
                 using PT = typename decltype(pt)::type;
-                return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+                return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
                     constexpr int kMax = MaxBlock<T, decltype(rt)::value, decltype(cpt)::value>::value;
                     if (p.block > kMax || p.block < 1) return hipErrorInvalidConfiguration;
                     return launch(rms_bwd_kernel<T, PT, decltype(mode)::value, decltype(cpt)::value,
                                                  decltype(rt)::value, decltype(pf)::value, decltype(var)::value,
-                                                 decltype(pg)::value>,
+                                                 decltype(pg)::value, decltype(lay)::value>,
                                   dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                                   (const T*)dy, rstd, (const PT*)w, eps, (T*)dx, ws, g);
                 });
@@ -65,13 +65,13 @@ int resident_wgs_rms(bool backward, const Plan& p, int xdt, int pdt) {
     (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
-        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf) {
+        return dispatch_shape<T>(p, [&](auto mode, auto cpt, auto rt, auto pf, auto lay) {
             {
                 constexpr int M_ = decltype(mode)::value, C_ = decltype(cpt)::value;
-                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value;
+                constexpr int R_ = decltype(rt)::value, P_ = decltype(pf)::value, L_ = decltype(lay)::value;
                 // The Llama form decides the plan; the float32 forms use the same shapes.
-                const void* k = backward ? (const void*)rms_bwd_kernel<T, PT, M_, C_, R_, P_, 0, 1>
-                                         : (const void*)rms_fwd_kernel<T, PT, M_, C_, R_, P_, 0>;
+                const void* k = backward ? (const void*)rms_bwd_kernel<T, PT, M_, C_, R_, P_, 0, 1, L_>
+                                         : (const void*)rms_fwd_kernel<T, PT, M_, C_, R_, P_, 0, L_>;
                 n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
                 return hipSuccess;
             }

@@ -44,6 +44,43 @@ template <> struct ChunkOf<f16_t> { static constexpr int value = 8; };
 template <typename T, int MODE>
 struct Elems { static constexpr int value = (MODE == MODE_SCALAR) ? 1 : ChunkOf<T>::value; };
 
+// Strided row operands (layout 1 kernels).  The M rows are the index space of up to three
+// leading dimensions of sizes (s0, d1, d2), the last fastest: row r is (i0, i1, i2) with
+// i2 = r mod d2, i1 = (r div d2) mod d1, i0 = r div (d2 d1); operand k's row starts st[k][0] i0 +
+// st[k][1] i1 + st[k][2] i2 elements past its base, and its N elements are contiguous.  The
+// divisions are multiplications by precomputed reciprocals (exact for r < 2^31: see
+// make_divisor), since rows are mapped once per tile.
+enum RowOperand { OP_X = 0, OP_DY = 1, OP_OUT = 2 };
+
+struct Divisor {
+    uint64_t m;   // ceil(2^sh / d)
+    int sh;       // 31 + ceil(log2 d)
+    uint32_t d;
+};
+
+// floor(n / d) for n < 2^31: with 2^l >= d and m = ceil(2^(31+l) / d) = (2^(31+l) + e) / d,
+// 0 <= e < d, n m / 2^(31+l) = n / d + n e / (d 2^(31+l)), and the second term is below 1/d
+// because n e < 2^31 2^l; floor(n / d) + frac <= floor(n / d) + (d - 1) / d, so the sum stays
+// below the next integer.  m <= 2^32, so n m < 2^63.
+__host__ __device__ inline Divisor make_divisor(uint32_t d) {
+    int l = 0;
+    while (l < 31 && (uint64_t(1) << l) < d) ++l;
+    Divisor v;
+    v.d = d;
+    v.sh = 31 + l;
+    v.m = ((uint64_t(1) << v.sh) + d - 1) / d;
+    return v;
+}
+__host__ __device__ inline uint32_t div_by(uint32_t n, const Divisor& v) {
+    return (uint32_t)(((uint64_t)n * v.m) >> v.sh);
+}
+
+struct RowMap {
+    Divisor d1, d2;
+    int64_t st[3][3];    // [operand][leading dimension] element strides
+    int64_t span[3];     // bytes from an operand's base to the end of its last row
+};
+
 // Launch geometry shared by all row kernels (values computed by the host planner).
 struct Geom {
     int64_t M, N;
@@ -60,7 +97,27 @@ struct Geom {
     int xcd_remap;    // 1: renumber workgroups so consecutive numbers share an XCD (grid % 8 == 0)
     float inv_n;      // 1 / N
     float w_offset;   // RMSNorm: added to the weight in float32 (1 for the (1 + weight) form)
+    int64_t pitch;    // SHIFTED: elements between consecutive rows' starts, for their shifts (N;
+                      // 0 for strided operands, whose rows all share the base's shift)
+    int64_t ps0, ps1; // element strides of the first and second parameter vectors
+    RowMap rm;        // strided operands (layout 1 kernels)
 };
+
+// Element offset of row `row` in operand `op`: row * N for dense [M, N] operands (LAY 0), the
+// row map's for strided ones (LAY 1).
+template <int LAY>
+__device__ __forceinline__ int64_t row_base(const Geom& g, int op, int64_t row) {
+    if constexpr (LAY == 0) {
+        return row * g.N;
+    } else {
+        const uint32_t r = (uint32_t)row;
+        const uint32_t q = div_by(r, g.rm.d2);
+        const uint32_t i2 = r - q * g.rm.d2.d;
+        const uint32_t i0 = div_by(q, g.rm.d1);
+        const uint32_t i1 = q - i0 * g.rm.d1.d;
+        return (int64_t)i0 * g.rm.st[op][0] + (int64_t)i1 * g.rm.st[op][1] + (int64_t)i2 * g.rm.st[op][2];
+    }
+}
 
 // ------------------------------------------------------------------------- conversions
 
@@ -177,12 +234,13 @@ struct RowRegs {
 // One descriptor covers one row tile of one tensor: its base is the tile's first element
 // (SHIFTED: the 16-byte block holding it), its record count the bytes from there to the
 // tensor's end (rounded up to 16: the aligned block that holds the last element), capped at
-// 1 GiB -- a tile spans at most 16 rows of 16384 float32, far less.
+// just below the out-of-range marker (2 GiB; a dense tile spans at most 16 rows of 16384
+// float32, far less).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOutOfRange = 0x80000000u;   // above every record count
-constexpr int64_t kMaxRecords = int64_t(1) << 30;
+constexpr int64_t kMaxRecords = int64_t(kOutOfRange) - 16;
 constexpr int kBufferFormat = 0x00020000;       // descriptor word 3: 32-bit data format
 constexpr int kNontemporal = 2;                 // cache policy: streaming (nt)
 
@@ -217,13 +275,22 @@ struct TileSrc {
     int64_t e0;
 };
 
-template <typename T, int MODE>
-__device__ __forceinline__ TileSrc tile_src(const T* __restrict__ p, int64_t row0, int64_t M, int64_t N,
-                                            int base_shift, bool live) {
+// Dense operands (LAY 0) get one descriptor per row tile.  Strided operands (LAY 1) get one
+// over the operand's whole span (at most kMaxRecords bytes, which the host checks): their rows
+// need not lie in order, and every row shares the base's shift.
+template <typename T, int MODE, int LAY = 0>
+__device__ __forceinline__ TileSrc tile_src(const T* __restrict__ p, int64_t row0, const Geom& g, int op,
+                                            bool live) {
     constexpr int V = Elems<T, MODE>::value;
-    int64_t e0 = row0 * N;
-    if (MODE == MODE_SHIFTED) e0 -= (e0 + base_shift) % V;
-    int64_t bytes = (M * N - e0) * (int64_t)sizeof(T);
+    int64_t e0, bytes;
+    if constexpr (LAY == 0) {
+        e0 = row0 * g.N;
+        if (MODE == MODE_SHIFTED) e0 -= (e0 + g.base_shift) % V;
+        bytes = (g.M * g.N - e0) * (int64_t)sizeof(T);
+    } else {
+        e0 = MODE == MODE_SHIFTED ? -(int64_t)g.base_shift : 0;
+        bytes = g.rm.span[op] - e0 * (int64_t)sizeof(T);
+    }
     bytes = (bytes + 15) & ~int64_t(15);
     TileSrc t;
     t.rsrc = make_rsrc(reinterpret_cast<const char*>(p) + e0 * (int64_t)sizeof(T), live ? bytes : 0);
@@ -241,18 +308,17 @@ __device__ __forceinline__ float load_stat(Rsrc r, int64_t row, int64_t row0, bo
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-// Load the CPT chunks of row `row` (row pitch N) from the tile source; columns outside the row
-// read as 0, and `rowvalid` false reads zeros.  Every chunk is one 16-byte load (SCALAR: one
+// Load the CPT chunks of the row starting at element rb (row_base) from the tile source; columns
+// outside the row read as 0, and `rowvalid` false reads zeros.  Every chunk is one 16-byte load (SCALAR: one
 // element).  A SHIFTED chunk cut by the row's ends holds elements of the neighbouring row (or,
 // at the tensor's ends, bytes of the 16-byte block beyond it), which are zeroed after the load.
 template <typename T, int MODE, int CPT>
-__device__ __forceinline__ void load_row(const TileSrc& src, int64_t row, int64_t N,
-                                         const ColMap<T, MODE, CPT>& cm, bool rowvalid,
-                                         RowRegs<T, MODE, CPT>& r) {
+__device__ __forceinline__ void load_row(const TileSrc& src, int64_t rb, const ColMap<T, MODE, CPT>& cm,
+                                         bool rowvalid, RowRegs<T, MODE, CPT>& r) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const bool in = rowvalid && cm.any[k];
-        const uint32_t off = lane_offset(in, (uint32_t)((row * N + cm.col0[k] - src.e0) * (int64_t)sizeof(T)));
+        const uint32_t off = lane_offset(in, (uint32_t)((rb + cm.col0[k] - src.e0) * (int64_t)sizeof(T)));
         if (MODE == MODE_SCALAR) {
             if constexpr (sizeof(T) == 4)
                 r.w[k][0] = __builtin_amdgcn_raw_buffer_load_b32(src.rsrc, off, 0, 0);
@@ -309,7 +375,8 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* o) {
     }
 }
 
-// Store chunk k of row `row` (row pitch N) into the tile destination d, from V float32 values
+// Store chunk k of the row starting at element rb (row_base; N elements) into the tile
+// destination d, from V float32 values
 // rounded to T; only columns inside the row are written, nothing when `rowvalid` is false.  A
 // whole chunk is one nontemporal 16-byte store.  A SHIFTED chunk cut by the row's ends covers
 // bytes [a, b) of its aligned 16-byte block (the rest belongs to the neighbouring row); that
@@ -317,12 +384,12 @@ __device__ __forceinline__ u32x4 pack_chunk(const float* o) {
 // the next 16-byte boundary and up to three falling from there to b.  Every lane issues all
 // of these stores, with out-of-range offsets for the pieces it does not need.
 template <typename T, int MODE, int CPT>
-__device__ __forceinline__ void store_chunk(const TileSrc& d, int64_t row, int64_t N,
+__device__ __forceinline__ void store_chunk(const TileSrc& d, int64_t rb, int64_t N,
                                             const ColMap<T, MODE, CPT>& cm, int k, const float* o,
                                             bool rowvalid) {
     constexpr int V = ColMap<T, MODE, CPT>::V;
     constexpr int ES = (int)sizeof(T);
-    const uint32_t off = (uint32_t)((row * N + cm.col0[k] - d.e0) * (int64_t)ES);
+    const uint32_t off = (uint32_t)((rb + cm.col0[k] - d.e0) * (int64_t)ES);
     if constexpr (MODE == MODE_SCALAR) {
         const bool in = rowvalid && cm.any[k];
         if constexpr (ES == 4) store_b32(d, in, off, __builtin_bit_cast(uint32_t, o[0]));
@@ -370,16 +437,16 @@ __device__ __forceinline__ void store_chunk(const TileSrc& d, int64_t row, int64
     }
 }
 
-// Store chunk k of row `row` of p (row pitch N) with global stores under the row mask: a
-// whole chunk is one nontemporal 16-byte store, a SHIFTED chunk cut by the row's ends is
+// Store chunk k of the row of p starting at element rb with global stores under the row mask:
+// a whole chunk is one nontemporal 16-byte store, a SHIFTED chunk cut by the row's ends is
 // written element by element.
 template <typename T, int MODE, int CPT>
-__device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t row, int64_t N,
+__device__ __forceinline__ void store_chunk(T* __restrict__ p, int64_t rb, int64_t N,
                                             const ColMap<T, MODE, CPT>& cm, int k, const float* o,
                                             bool rowvalid) {
     constexpr int V = ColMap<T, MODE, CPT>::V;
     if (!rowvalid || !cm.any[k]) return;
-    T* rp = p + row * N + cm.col0[k];
+    T* rp = p + rb + cm.col0[k];
     if constexpr (MODE == MODE_SCALAR) {
         *rp = from_f32<T>(o[0]);
     } else if (MODE == MODE_ALIGNED || cm.full[k]) {
@@ -399,17 +466,18 @@ template <int MODE, int CPT, bool BWD>
 constexpr bool kBufferStores = BWD && MODE == MODE_ALIGNED && CPT >= 2;
 
 template <typename T, int MODE, int CPT, bool BUF>
-__device__ __forceinline__ void put_chunk(T* __restrict__ p, const TileSrc& d, int64_t row, int64_t N,
+__device__ __forceinline__ void put_chunk(T* __restrict__ p, const TileSrc& d, int64_t rb, int64_t N,
                                           const ColMap<T, MODE, CPT>& cm, int k, const float* o,
                                           bool rowvalid) {
-    if constexpr (BUF) store_chunk<T, MODE, CPT>(d, row, N, cm, k, o, rowvalid);
-    else store_chunk<T, MODE, CPT>(p, row, N, cm, k, o, rowvalid);
+    if constexpr (BUF) store_chunk<T, MODE, CPT>(d, rb, N, cm, k, o, rowvalid);
+    else store_chunk<T, MODE, CPT>(p, rb, N, cm, k, o, rowvalid);
 }
 
 
-// Load a per-column parameter vector for this thread's columns (0 outside [0, N)).
+// Load a per-column parameter vector (element stride ps) for this thread's columns (0 outside
+// [0, N)).
 template <typename T, typename PT, int MODE, int CPT>
-__device__ __forceinline__ void load_param(const PT* __restrict__ p, int64_t N,
+__device__ __forceinline__ void load_param(const PT* __restrict__ p, int64_t N, int64_t ps,
                                            const ColMap<T, MODE, CPT>& cm, float* o) {
     constexpr int V = ColMap<T, MODE, CPT>::V;
 #pragma unroll
@@ -417,7 +485,7 @@ __device__ __forceinline__ void load_param(const PT* __restrict__ p, int64_t N,
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             int j = cm.col0[k] + v;
-            o[k * V + v] = (j >= 0 && (int64_t)j < N && cm.any[k]) ? to_f32(p[j]) : 0.f;
+            o[k * V + v] = (j >= 0 && (int64_t)j < N && cm.any[k]) ? to_f32(p[j * ps]) : 0.f;
         }
 }
 

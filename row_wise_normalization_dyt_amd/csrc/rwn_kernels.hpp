@@ -72,7 +72,7 @@ struct RowCtx {
             // launcher makes rpp, or the tile stride times rpp, a multiple of V), so the first
             // row fixes the shift.
             const int64_t r0 = t_begin * rows_per_tile + slot;
-            s = (int)(((int64_t)g.base_shift + r0 * g.N) % ColMap<T, MODE, CPT>::V);
+            s = (int)(((int64_t)g.base_shift + r0 * g.pitch) % ColMap<T, MODE, CPT>::V);
         }
         cm.init(lane, g.tpr, g.N, s, cblk * g.tpr * CPT);
     }
@@ -140,11 +140,11 @@ __device__ __forceinline__ void tile_loop(const Ctx& c, Fetch&& fetch, Body&& bo
 
 // Load a per-column parameter (or `dflt` for every column when p is NULL).
 template <typename T, typename PT, int MODE, int CPT>
-__device__ __forceinline__ void load_param_or(const PT* __restrict__ p, float dflt, int64_t N,
+__device__ __forceinline__ void load_param_or(const PT* __restrict__ p, float dflt, int64_t N, int64_t ps,
                                               const ColMap<T, MODE, CPT>& cm, float* o) {
     constexpr int E = CPT * ColMap<T, MODE, CPT>::V;
     if (p) {
-        load_param<T, PT, MODE, CPT>(p, N, cm, o);
+        load_param<T, PT, MODE, CPT>(p, N, ps, cm, o);
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = dflt;
@@ -251,7 +251,7 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t c
 
 // ================================================================================== DyT
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, const PT* __restrict__ beta, T* __restrict__ y,
@@ -260,8 +260,8 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
     constexpr int E = CPT * V;
     RowCtx<T, MODE, CPT, RT> c(g);
     float ga[E], be[E];
-    load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
-    load_param<T, PT, MODE, CPT>(beta, g.N, c.cm, be);
+    load_param<T, PT, MODE, CPT>(gamma, g.N, g.ps0, c.cm, ga);
+    load_param<T, PT, MODE, CPT>(beta, g.N, g.ps1, c.cm, be);
     const float alpha = to_f32(alpha_p[0]);
     struct In {
         RowRegs<T, MODE, CPT> xr[RT];
@@ -273,9 +273,9 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
         c.tile_rows(tile, g, in.row, in.ok);
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, tile < c.t_end);
 #pragma unroll
-        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
     };
     auto body = [&](const In& in) {
 #pragma unroll
@@ -286,7 +286,7 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
 #pragma unroll
                 for (int v = 0; v < V; ++v)
                     o[v] = __builtin_fmaf(ga[k * V + v], tanh_only(alpha * in.xr[u].get(k, v)), be[k * V + v]);
-                store_chunk<T, MODE, CPT>(y, in.row[u], g.N, c.cm, k, o, in.ok[u]);
+                store_chunk<T, MODE, CPT>(y, row_base<LAY>(g, OP_OUT, in.row[u]), g.N, c.cm, k, o, in.ok[u]);
             }
         }
     };
@@ -295,7 +295,7 @@ dyt_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p,
 
 // PG 0: no parameter gradient is wanted; the kernel computes dx only (no column partials,
 // nothing written to the workspace, which may be NULL).
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
                const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws,
@@ -306,7 +306,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
     __shared__ float red[kRedFloats];
     RowCtx<T, MODE, CPT, RT> c(g);
     float ga[E];
-    load_param<T, PT, MODE, CPT>(gamma, g.N, c.cm, ga);
+    load_param<T, PT, MODE, CPT>(gamma, g.N, g.ps0, c.cm, ga);
     const float alpha = to_f32(alpha_p[0]);
     float acc_g[E], acc_b[E], acc_a = 0.f;
 #pragma unroll
@@ -323,12 +323,12 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
         const bool live = tile < c.t_end;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
-        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, live);
+        const TileSrc sg = tile_src<T, MODE, LAY>(dy, row0, g, OP_DY, live);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
-            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
+            load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, row_base<LAY>(g, OP_DY, in.row[u]), c.cm, in.ok[u], in.gr[u]);
         }
     };
     // With a finite alpha nothing a padded element computes can be NaN: its x, dy and gamma
@@ -338,7 +338,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
     const bool finite_alpha = __builtin_isfinite(alpha);
     constexpr bool BUF = kBufferStores<MODE, CPT, true>;
     auto body = [&](const In& in) {
-        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
+        const TileSrc dst = tile_src<T, MODE, LAY>(dx, in.row0, g, OP_OUT, true);
         auto rows = [&](auto finite) {
 #pragma unroll
             for (int u = 0; u < RT; ++u) {
@@ -370,7 +370,7 @@ dyt_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __re
                             o[v] = d * as;
                         }
                     }
-                    put_chunk<T, MODE, CPT, BUF>(dx, dst, in.row[u], g.N, c.cm, k, o, in.ok[u]);
+                    put_chunk<T, MODE, CPT, BUF>(dx, dst, row_base<LAY>(g, OP_OUT, in.row[u]), g.N, c.cm, k, o, in.ok[u]);
                 }
             }
         };
@@ -435,7 +435,7 @@ __device__ __forceinline__ void ln_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
     for (int u = 0; u < RT; ++u) rs[u] = __builtin_amdgcn_rsqf(s[u] * g.inv_n + eps);
 }
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* __restrict__ beta,
               float eps, T* __restrict__ y, float* __restrict__ mean_out,
@@ -446,8 +446,8 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
     int parity = 0;
     RowCtx<T, MODE, CPT, RT> c(g);
     float ga[E], be[E];
-    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
-    load_param_or<T, PT, MODE, CPT>(beta, 0.f, g.N, c.cm, be);
+    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, g.ps0, c.cm, ga);
+    load_param_or<T, PT, MODE, CPT>(beta, 0.f, g.N, g.ps1, c.cm, be);
     struct In {
         RowRegs<T, MODE, CPT> xr[RT];
         int64_t row[RT];
@@ -458,9 +458,9 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
         c.tile_rows(tile, g, in.row, in.ok);
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, tile < c.t_end);
 #pragma unroll
-        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
     };
     auto body = [&](const In& in) {
         float mu[RT], rs[RT];
@@ -473,7 +473,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
 #pragma unroll
                 for (int v = 0; v < V; ++v)
                     o[v] = __builtin_fmaf((in.xr[u].get(k, v) - mu[u]) * rs[u], ga[k * V + v], be[k * V + v]);
-                store_chunk<T, MODE, CPT>(y, in.row[u], g.N, c.cm, k, o, in.ok[u]);
+                store_chunk<T, MODE, CPT>(y, row_base<LAY>(g, OP_OUT, in.row[u]), g.N, c.cm, k, o, in.ok[u]);
             }
             if (in.ok[u] && c.lane == 0) {
                 if (mean_out) mean_out[in.row[u]] = mu[u];
@@ -486,7 +486,7 @@ ln_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ gamma, const PT* _
 
 // PG: which parameter-gradient partials are accumulated and written (bit 0: dgamma, bit 1:
 // dbeta; 0: dx only, the workspace may be NULL).
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int PG, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ mean_in,
               const float* __restrict__ rstd_in, const PT* __restrict__ gamma, float eps,
@@ -498,7 +498,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
     int parity = 0;
     RowCtx<T, MODE, CPT, RT> c(g);
     float ga[E];
-    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, c.cm, ga);
+    load_param_or<T, PT, MODE, CPT>(gamma, 1.f, g.N, g.ps0, c.cm, ga);
     const bool have_stats = mean_in != nullptr && rstd_in != nullptr;
     float acc_g[E], acc_b[E];
 #pragma unroll
@@ -516,14 +516,14 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
         const bool live = tile < c.t_end;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
-        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, live);
+        const TileSrc sg = tile_src<T, MODE, LAY>(dy, row0, g, OP_DY, live);
         const Rsrc sm = stats_src(mean_in, row0, g.M, live && have_stats);
         const Rsrc sr = stats_src(rstd_in, row0, g.M, live && have_stats);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
-            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
+            load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, row_base<LAY>(g, OP_DY, in.row[u]), c.cm, in.ok[u], in.gr[u]);
             in.mu[u] = load_stat(sm, in.row[u], row0, in.ok[u]);
             in.rs[u] = load_stat(sr, in.row[u], row0, in.ok[u]);
         }
@@ -534,7 +534,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
         const auto& ok = in.ok;
         const auto& row = in.row;
         constexpr bool BUF = kBufferStores<MODE, CPT, true>;
-        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
+        const TileSrc dst = tile_src<T, MODE, LAY>(dx, in.row0, g, OP_OUT, true);
         float mu[RT], rs[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
@@ -582,7 +582,7 @@ ln_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __
                     if constexpr (PG & 2) acc_b[e] += gv;
                     o[v] = rs[u] * (gv * ga[e] - c1 - xh * c2);
                 }
-                put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
+                put_chunk<T, MODE, CPT, BUF>(dx, dst, row_base<LAY>(g, OP_OUT, row[u]), g.N, c.cm, k, o, ok[u]);
             }
         }
     };
@@ -834,7 +834,7 @@ __device__ __forceinline__ void rms_stats(const RowRegs<T, MODE, CPT> (&xr)[RT],
 
 // VAR 0: the Llama form (normalized value rounded to x's dtype, then the weight multiply);
 // VAR 1: weight (plus g.w_offset) times the float32 normalized value, rounded once.
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value)))
 rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps,
                T* __restrict__ y, float* __restrict__ rstd_out, Geom g) {
@@ -844,7 +844,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
     int parity = 0;
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
-    load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    load_param<T, PT, MODE, CPT>(weight, g.N, g.ps0, c.cm, w);
     if constexpr (VAR != 0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) w[e] += g.w_offset;   // (1 + weight) in float32
@@ -859,9 +859,9 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
         c.tile_rows(tile, g, in.row, in.ok);
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, tile < c.t_end);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, tile < c.t_end);
 #pragma unroll
-        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
+        for (int u = 0; u < RT; ++u) load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
     };
     auto body = [&](const In& in) {
         const auto& xr = in.xr;
@@ -882,7 +882,7 @@ rms_fwd_kernel(const T* __restrict__ x, const PT* __restrict__ weight, float eps
                     const float h = xr[u].get(k, v) * rs[u];
                     o[v] = w[k * V + v] * (VAR == 0 ? round_through<T>(h) : h);
                 }
-                store_chunk<T, MODE, CPT>(y, row[u], g.N, c.cm, k, o, ok[u]);
+                store_chunk<T, MODE, CPT>(y, row_base<LAY>(g, OP_OUT, row[u]), g.N, c.cm, k, o, ok[u]);
             }
             if (ok[u] && c.lane == 0 && rstd_out) rstd_out[row[u]] = rs[u];
         }
@@ -897,7 +897,7 @@ template <int MODE, int CPT> struct RmsBwdWaves {
     static constexpr int value = (MODE == MODE_SHIFTED && CPT == 1) ? 5 : 1;
 };
 
-template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR, int PG>
+template <typename T, typename PT, int MODE, int CPT, int RT, int PF, int VAR, int PG, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(1, MaxBlock<T, RT, CPT>::value),
                                amdgpu_waves_per_eu(RmsBwdWaves<MODE, CPT>::value)))
 rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* __restrict__ rstd_in,
@@ -910,7 +910,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
     int parity = 0;
     RowCtx<T, MODE, CPT, RT> c(g);
     float w[E];
-    load_param<T, PT, MODE, CPT>(weight, g.N, c.cm, w);
+    load_param<T, PT, MODE, CPT>(weight, g.N, g.ps0, c.cm, w);
     if constexpr (VAR != 0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) w[e] += g.w_offset;   // (1 + weight) in float32
@@ -931,13 +931,13 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
         const int64_t row0 = tile * c.rows_per_tile;
         in.row0 = row0;
         const bool live = tile < c.t_end;
-        const TileSrc sx = tile_src<T, MODE>(x, row0, g.M, g.N, g.base_shift, live);
-        const TileSrc sg = tile_src<T, MODE>(dy, row0, g.M, g.N, g.base_shift, live);
+        const TileSrc sx = tile_src<T, MODE, LAY>(x, row0, g, OP_X, live);
+        const TileSrc sg = tile_src<T, MODE, LAY>(dy, row0, g, OP_DY, live);
         const Rsrc sr = stats_src(rstd_in, row0, g.M, live);
 #pragma unroll
         for (int u = 0; u < RT; ++u) {
-            load_row<T, MODE, CPT>(sx, in.row[u], g.N, c.cm, in.ok[u], in.xr[u]);
-            load_row<T, MODE, CPT>(sg, in.row[u], g.N, c.cm, in.ok[u], in.gr[u]);
+            load_row<T, MODE, CPT>(sx, row_base<LAY>(g, OP_X, in.row[u]), c.cm, in.ok[u], in.xr[u]);
+            load_row<T, MODE, CPT>(sg, row_base<LAY>(g, OP_DY, in.row[u]), c.cm, in.ok[u], in.gr[u]);
             in.rs[u] = load_stat(sr, in.row[u], row0, in.ok[u]);
         }
     };
@@ -947,7 +947,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
         const auto& ok = in.ok;
         const auto& row = in.row;
         constexpr bool BUF = kBufferStores<MODE, CPT, true>;
-        const TileSrc dst = tile_src<T, MODE>(dx, in.row0, g.M, g.N, g.base_shift, true);
+        const TileSrc dst = tile_src<T, MODE, LAY>(dx, in.row0, g, OP_OUT, true);
         float rs[RT];
 #pragma unroll
         for (int u = 0; u < RT; ++u) rs[u] = in.rs[u];
@@ -994,7 +994,7 @@ rms_bwd_kernel(const T* __restrict__ x, const T* __restrict__ dy, const float* _
                     }
                     o[v] = rs[u] * (gg - h * cc);
                 }
-                put_chunk<T, MODE, CPT, BUF>(dx, dst, row[u], g.N, c.cm, k, o, ok[u]);
+                put_chunk<T, MODE, CPT, BUF>(dx, dst, row_base<LAY>(g, OP_OUT, row[u]), g.N, c.cm, k, o, ok[u]);
             }
         }
     };

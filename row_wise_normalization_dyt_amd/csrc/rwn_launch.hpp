@@ -46,17 +46,23 @@ struct Plan {
     int64_t ws_cs = 0;
     size_t lds_bytes = 0;     // dynamic LDS of the backward stage 1
     int64_t M = 0, N = 0;
+    int layout = 0;           // row operands: 0 dense [M, N]; 1 strided, every row 16-byte chunks
+                              // at one shift; 2 strided, element by element (SCALAR)
+    int64_t ps0 = 1, ps1 = 1; // parameter vectors' element strides
+    RowMap rm{};              // strided row map (layouts 1 and 2), filled in by the caller
 
     int64_t partial_rows() const { return grid / ncb; }
 };
 
 // Plan for one call.  misalign_bytes: address of the [M, N] operands modulo 16 (a multiple of
-// the element size).  cus: compute units of the device.  pdt: the parameter dtype, or -1 when
+// the element size).  layout: 0 for dense [M, N] operands; 1 for strided operands whose rows
+// all start misalign_bytes past a 16-byte boundary; 2 for strided operands of any alignment
+// (SCALAR).  Strided plans run the general kernels with one row per thread, no pipelining.  cus: compute units of the device.  pdt: the parameter dtype, or -1 when
 // the plan must hold for every parameter dtype of x's dtype (the workspace query).  occupancy:
 // ask the runtime how many workgroups of the chosen kernel fit on a CU (needs a current device;
 // false plans from launch bounds alone).  Returns false if N is too wide.
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
-               int cus, bool occupancy, Plan* out);
+               int cus, bool occupancy, Plan* out, int layout = 0);
 
 // Workgroups of the plan's kernel that fit on one CU at once (registers, LDS, wave slots), from
 // the runtime; 0 if unknown.  One function per layer, defined beside that layer's launchers.
@@ -89,6 +95,10 @@ inline Geom make_geom(const Plan& p) {
     g.base_shift = p.base_shift;
     g.inv_n = 1.0f / (float)p.N;
     g.w_offset = 0.0f;
+    g.pitch = p.layout ? 0 : p.N;
+    g.ps0 = p.ps0;
+    g.ps1 = p.ps1;
+    g.rm = p.rm;
     return g;
 }
 
@@ -125,8 +135,8 @@ hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
     return hipErrorInvalidValue;
 }
 
-// Calls f(IC<MODE>, IC<CPT>, IC<RT>, IC<PF>) for the instantiated shapes.  The pipelined
-// tile loop (PF = 1) exists for shapes with at most two chunks per thread per tensor.
+// The pipelined tile loop (PF = 1) exists for shapes with at most two chunks per thread per
+// tensor.
 template <typename F>
 hipError_t dispatch_pf(const Plan& p, F&& f) {
     return p.pf ? f(IC<1>{}) : f(IC<0>{});
@@ -138,27 +148,48 @@ hipError_t dispatch_pf2(const Plan& p, F&& f) {
     return p.pf == 2 ? f(IC<2>{}) : p.pf ? f(IC<1>{}) : f(IC<0>{});
 }
 
+// Calls f(IC<MODE>, IC<CPT>, IC<RT>, IC<PF>, IC<LAY>) for the instantiated shapes.  Strided
+// plans (LAY 1: layouts 1 and 2) exist with one row per thread and no pipelining.
 template <typename T, typename F>
 hipError_t dispatch_shape(const Plan& p, F&& f) {
     if ((p.pf && p.cpt * p.rt > 2) || (p.pf == 2 && (p.cpt * p.rt != 1 || p.mode == MODE_SCALAR)))
         return hipErrorInvalidValue;
+    if (p.layout) {
+        if (p.rt != 1 || p.pf != 0) return hipErrorInvalidValue;
+        auto by_cpt = [&](auto mode) {
+            if (p.cpt == 1) return f(mode, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{});
+            if (p.cpt == 2) return f(mode, IC<2>{}, IC<1>{}, IC<0>{}, IC<1>{});
+            if (p.cpt == 4) return f(mode, IC<4>{}, IC<1>{}, IC<0>{}, IC<1>{});
+            return hipErrorInvalidValue;
+        };
+        if (p.mode == MODE_ALIGNED) return by_cpt(IC<MODE_ALIGNED>{});
+        if (p.mode == MODE_SHIFTED) return by_cpt(IC<MODE_SHIFTED>{});
+        return by_cpt(IC<MODE_SCALAR>{});
+    }
+    const IC<0> dense;
     if (p.mode == MODE_ALIGNED) {
-        if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{}, IC<0>{});
+        if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{}, IC<0>{}, dense);
         if (p.rt == 2 && p.cpt == 1)
-            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{}, pf); });
+            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{}, pf, dense); });
         if (p.rt == 1) {
-            if (p.cpt == 1) return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf); });
-            if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{}, pf); });
-            if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{}, IC<0>{});
+            if (p.cpt == 1)
+                return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf, dense); });
+            if (p.cpt == 2)
+                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{}, pf, dense); });
+            if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
         }
     } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
-        if (p.cpt == 1) return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf); });
-        if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{}, pf); });
-        if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{}, IC<0>{});
+        if (p.cpt == 1)
+            return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf, dense); });
+        if (p.cpt == 2)
+            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{}, pf, dense); });
+        if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
     } else if (p.mode == MODE_SCALAR && p.rt == 1) {
-        if (p.cpt == 1) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{}, pf); });
-        if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{}, pf); });
-        if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{}, IC<0>{});
+        if (p.cpt == 1)
+            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{}, pf, dense); });
+        if (p.cpt == 2)
+            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{}, pf, dense); });
+        if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
     }
     return hipErrorInvalidValue;
 }

@@ -178,6 +178,75 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
                     assert p["kt"] == 1
 
 
+@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("backward", [False, True])
+def test_strided_plans(layout, backward):
+    """Strided operands take the general kernels with one row per thread and no pipelining;
+    layout 2 (rows of mixed alignment) moves elements (SCALAR), and LayerNorm / RMSNorm take
+    it up to 2048 16-bit or 4096 float32 elements, DyT at any width through column blocks."""
+    for dtype, esz in ((torch.float32, 4), (torch.bfloat16, 2), (torch.float16, 2)):
+        V = 16 // esz
+        for N in (1, 7, 24, 128, 129, 1025, 2048, 2049, 4096, 4097, 16384):
+            for mis in (range(0, 16, esz) if layout == 1 else (0,)):
+                for layer in ("dyt", "layernorm", "rmsnorm"):
+                    limit = 4096 if esz == 4 else 2048
+                    if layout == 2 and layer != "dyt" and N > limit:
+                        with pytest.raises(rwn.RwnError, match="UNSUPPORTED"):
+                            rwn.plan(layer, backward, 4099, N, dtype, mis, cus=256, layout=layout)
+                        continue
+                    if layout == 1 and (N % V or mis) and N > 16384 - (V - 1) and layer != "dyt":
+                        # a row that straddles one more chunk than the widest aligned row
+                        with pytest.raises(rwn.RwnError, match="UNSUPPORTED"):
+                            rwn.plan(layer, backward, 4099, N, dtype, mis, cus=256, layout=layout)
+                        continue
+                    p = rwn.plan(layer, backward, 4099, N, dtype, mis, cus=256, layout=layout)
+                    assert p["rt"] == 1 and p["prefetch"] == 0 and p["flat"] == 0 and p["split"] == 0, p
+                    if layout == 2:
+                        assert p["mode"] == 2 and p["vec"] == 1, p
+                    else:
+                        assert p["mode"] == (0 if (N % V == 0 and mis == 0) else p["mode"]), p
+                    chunks = N if p["mode"] == 2 else -(-(N + (V - 1 if p["mode"] == 1 else 0)) // V)
+                    assert p["tpr"] * p["cpt"] * p["ncb"] >= chunks, p
+                    assert p["cpt"] == 1 or layer != "dyt", p
+                    cap = 512 if (p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2)) else 1024
+                    assert p["block"] <= cap and p["ntiles"] * p["rpp"] >= 4099 > (p["ntiles"] - 1) * p["rpp"], p
+
+
+def test_strided_argument_errors(lib):
+    """The strided entry points validate leading sizes, strides, spans and output overlap
+    before touching a device."""
+    A = ctypes.c_int64 * 3
+    lead, xs, ys = A(4, 0, 0), A(64, 0, 0), A(64, 0, 0)
+
+    def fwd(nlead=1, lead=lead, N=64, x=P, x_str=xs, y=P, y_str=ys, xdt=0, gstride=1):
+        return lib.dyt_fwd_strided(nlead, lead, N, x, x_str, xdt, P, P, gstride, P, 1, 0, y, y_str, None)
+
+    for n in (0, 4):
+        assert fwd(nlead=n) == 1 and "nlead" in _err(lib)
+    assert fwd(lead=None) == 1
+    assert fwd(lead=A(-1, 0, 0)) == 1 and "negative" in _err(lib)
+    assert fwd(x_str=A(-64, 0, 0)) == 1 and "negative" in _err(lib)
+    assert fwd(x_str=None) == 1 and "strides" in _err(lib)
+    assert fwd(gstride=-1) == 1 and "parameter strides" in _err(lib)
+    assert fwd(y_str=A(0, 0, 0)) == 1 and "overlap" in _err(lib)           # four rows on one row
+    assert fwd(y_str=A(63, 0, 0)) == 1 and "overlap" in _err(lib)          # rows 63 apart, 64 wide
+    assert fwd(nlead=2, lead=A(4, 8, 0), y_str=A(8 * 64, 32, 0)) == 1 and "overlap" in _err(lib)
+    assert fwd(x_str=A(1 << 40, 0, 0)) == 2 and "spans" in _err(lib)
+    assert fwd(nlead=2, lead=A(1 << 16, 1 << 16, 0), x_str=A(0, 0, 0)) == 2 and "rows" in _err(lib)
+    assert fwd(x=ctypes.c_void_p(18)) == 1 and "aligned" in _err(lib)      # float32 at 2 mod 4
+    assert fwd(N=16385) == 2
+    # no rows: nothing to read or write, and no device is needed
+    assert fwd(lead=A(0, 0, 0), x=None, y=None) == 0
+    assert lib.layernorm_fwd_strided(2, A(0, 5, 0), 8, None, A(8, 40, 0), 1, None, 1, None, 1, 0, 1e-5, None,
+                                     A(8, 40, 0), None, None, None) == 0
+    bad = A(-1, 0, 0)
+    assert lib.layernorm_bwd_strided(1, lead, 64, P, xs, P, bad, 0, None, None, P, 1, 0, 1e-5, P, ys, None, None,
+                                     None, 0, None) == 1
+    assert lib.rmsnorm_bwd_strided(1, lead, 64, P, xs, P, xs, 0, None, P, 1, 0, 1e-6, 0, P, A(0, 0, 0), None, None,
+                                   0, None) == 1
+    assert lib.rmsnorm_fwd_strided(1, lead, 64, P, xs, 0, P, -2, 0, 1e-6, 0, P, ys, None, None) == 1
+
+
 def test_plan_uses_narrow_tiles_for_narrow_rows():
     p = rwn.plan("layernorm", True, 401408, 24, torch.float32, cus=256)
     assert p["mode"] == 0 and p["tpr"] == 8 and p["rpp"] == 32
