@@ -24,10 +24,12 @@
  *          backward whose gamma/beta gradients are column sums over M rows.  Read as
  *          torch.nn.LayerNorm: biased variance, eps inside the square root, affine gamma, beta.
  *   [RMS]  DeepSpeed PR #8645 (embedded in PR #8664), sections "Summary" and "Semantics": the
- *          expression weight * (x.float() * rsqrt(mean(x.float()**2) + eps)).to(x.dtype), FP32
- *          statistics, one rounding of the normalized value to the input dtype, then the weight
- *          multiply; in the backward grad_out*weight is rounded to the input dtype before use,
- *          and grad_out*normalized is rounded before its column sum.
+ *          Llama expression weight * (x.float() * rsqrt(mean(x.float()**2) + eps)).to(x.dtype).
+ *          Read here as: statistics in float32; the normalized row is stored in x's dtype before
+ *          the weight touches it; in the backward the upstream gradient times the weight is
+ *          stored in x's dtype before it is used, and each weight-gradient term (upstream
+ *          gradient times normalized value) is stored in the weight gradient's dtype before the
+ *          float32 column sum.
  *   [W1]   DeepSpeed PR #8664, commit messages and "Numerics": at width one the pre-gamma input
  *          derivative of RMSNorm is eps / (x^2 + eps)^(3/2).
  *
