@@ -126,8 +126,7 @@ static void partial_layout(int layer, Plan& p) {
 
 // Split-row plan (rwn_split.hpp) for a wide row: W <= max_w waves per row
 // slot and CPT whole chunks per lane covering the row's aligned middle, head and tail elements as
-// scalar slots (measured at 65536 x 1025 bf16, against one chunk per lane: DyT forward 73.0 ->
-// 59.9 us, RMSNorm backward 87.3 -> 83.3 us; four per lane spill in backwards).  Slots fill
+// scalar slots.  Slots fill
 // 512-thread workgroups; a backward combines its
 // slots' partials in LDS (NG gradients x N floats) when that fits in 48 KB, else takes one slot
 // per workgroup.  Returns false where no shape fits (float32 rows wider than 8192), leaving the
@@ -140,23 +139,40 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     const int esz = xdt == DT_F32 ? 4 : 2;
     const int V = 16 / esz;
     const int64_t nm = N / V;   // most whole chunks a row can hold (a row starting aligned)
-    // Chunks per lane: 16 elements per lane (2 bfloat16 / float16 chunks, 4 float32 ones), or
-    // half that where it takes fewer lane slots; 32 elements only for LayerNorm / RMSNorm rows
-    // too wide for 8 waves otherwise (DyT's backward would spill: its wide rows keep the general
-    // kernels' column blocks).
-    const int pref = 16 / V;
+    // Chunks per lane, in order of preference; the fewest lane slots win and ties go to the
+    // earlier entry.  Measured at 65536 x {1025, 2049, 4097} bf16 and 65536 x 1025 float32
+    // (forward / backward us): LayerNorm and RMSNorm backwards run fastest with 8 elements per
+    // lane (bf16 N = 2049: 1 chunk 142.4 / 132.2 against 2 chunks 178.2 / 151.2; N = 4097: 286.2 /
+    // 275.5 against 356.9 / 302.6; float32 N = 1025: 2 chunks 149.7 / 147.2 against 4 chunks
+    // 154.6 / 153.3 and 1 chunk 212.3 / 156.7), their forwards with 2 chunks (bf16 N = 2049
+    // LayerNorm 105.5 against 118.9 with 1; float32 N = 1025 98.0 against 107.5 with 4), and DyT
+    // with 16 elements per lane (bf16 N = 2049 backward 178.5 against 183.4 with 1 chunk; float32
+    // N = 1025 forward 108.5 / backward 158.0 with 4 chunks against 113.5 / 174.4 with 2).  32
+    // elements per lane (4 bfloat16 chunks) only for LayerNorm / RMSNorm rows too wide for 8
+    // waves otherwise: DyT's backward would spill there.
+    int cands[3];
+    if (layer == LAYER_DYT) {
+        if (V == 8) { cands[0] = 2; cands[1] = 1; cands[2] = 4; }
+        else { cands[0] = 4; cands[1] = 2; cands[2] = 1; }
+    } else if (backward && V == 8) {
+        cands[0] = 1; cands[1] = 2; cands[2] = 4;
+    } else if (V == 8) {
+        cands[0] = 2; cands[1] = 1; cands[2] = 4;
+    } else {
+        cands[0] = 2; cands[1] = 4; cands[2] = 1;
+    }
     const bool wide_ok = layer != LAYER_DYT && max_w >= 8;   // rows no other plan takes
     int bw = 0, bc = 0;
     int64_t best_slots = -1;
-    const int cands[3] = {pref, pref / 2, pref * 2};
     for (int ci = 0; ci < 3; ++ci) {
         const int c = cands[ci];
-        if (c < 1 || c > 4 || (ci == 2 && !wide_ok)) continue;
+        const bool wide = c * V > 16;
+        if (wide && !wide_ok) continue;
         if (split_cpt > 0 && c != split_cpt) continue;
         const int64_t w = (nm + 64 * c - 1) / (64 * c);
         if (w > max_w) continue;
         const int64_t slots = 64 * w * c;
-        if (ci == 2 && bw) continue;   // only when nothing narrower fits
+        if (wide && bw) continue;   // only when nothing narrower fits
         if (best_slots < 0 || slots < best_slots) {
             best_slots = slots;
             bw = (int)w;
