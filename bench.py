@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the per-config parity spot checks")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming probes")
+    ap.add_argument("--probe-only", type=int, default=0, metavar="BYTES",
+                    help="run 3 launches of the one-in-one-out streaming probe over BYTES and exit (a "
+                         "known-size dispatch for calibrating HBM byte counters)")
     return ap.parse_args()
 
 
@@ -324,8 +327,9 @@ def config_entry(wl, r, parity):
          "ms_per_step_p10_p50_p90": [round(_pct(r["chunk_ms"], q), 5) for q in (0.1, 0.5, 0.9)],
          "fwd_ms": round(r["fwd_ms"], 5), "bwd_ms": round(r["bwd_ms"], 5),
          "kernel_ms_traced": {k: round(x["avg_ms"], 5) for k, x in r["kernels"].items()},
-         "dominant_kernel": {k: rl[k] for k in ("kernel", "avg_launch_ms", "frac", "untraced_call_ms",
-                                                "frac_untraced_call")},
+         "dominant_kernel": dict({k: rl[k] for k in ("kernel", "avg_launch_ms", "frac", "untraced_call_ms",
+                                                     "frac_untraced_call")},
+                                 traffic=traffic_for(wl, rl["kernel"])),
          "bytes_per_step": byts}
     if parity is not None:
         e["parity"] = parity
@@ -342,6 +346,15 @@ def main():
     import torch
     import workloads
     torch.cuda.set_device(0)
+    if args.probe_only:
+        import row_wise_normalization_dyt_amd as rwn
+        nb = (args.probe_only + 15) // 16 * 16
+        a, c = torch.ones(nb, dtype=torch.uint8, device="cuda"), torch.empty(nb, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            rwn.stream_probe(a, c, None, unroll=4, nontemporal=True, wg_per_cu=8)
+        torch.cuda.synchronize()
+        print(json.dumps({"probe_only_bytes": nb, "launches": 3}))
+        return
     name = args.workload or workloads.HEADLINE
     wl = workloads.WORKLOADS[name]
 
