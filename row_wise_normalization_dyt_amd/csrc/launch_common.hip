@@ -53,23 +53,31 @@ static int env_int(const char* name, int lo, int hi, int dflt) {
 }
 
 int kernel_occupancy(const void* kernel, int block, size_t dyn_lds) {
+    // Keyed by device as well: the answer is the current device's (devices of one process may
+    // differ in registers, LDS or wave slots).
     struct Key {
         const void* k;
+        int dev;
         int block;
         size_t lds;
         int n;
     };
     static std::mutex mu;
     static std::vector<Key> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
     std::lock_guard<std::mutex> lock(mu);
     for (const Key& e : cache)
-        if (e.k == kernel && e.block == block && e.lds == dyn_lds) return e.n;
+        if (e.k == kernel && e.dev == dev && e.block == block && e.lds == dyn_lds) return e.n;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, dyn_lds) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
-    cache.push_back(Key{kernel, block, dyn_lds, n});
+    cache.push_back(Key{kernel, dev, block, dyn_lds, n});
     return n;
 }
 

@@ -244,3 +244,37 @@ def test_swapped_modules_keep_the_originals_dtype_and_values(xdt):
                 ulp = 2.0 ** (-7 if xdt == torch.bfloat16 else -10)
                 err = ((out.float() - ref.float()).abs() / ref.float().abs().clamp_min(1e-3)).max().item()
                 assert err <= 4 * ulp, (type(o).__name__, wdt, err)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("layer", ["layernorm", "rmsnorm", "dyt"])
+def test_autograd_head_major_upstream_gradient(layer, monkeypatch):
+    """A q/k norm as attention uses it: x is [B, S, H, D] contiguous, the output is read transposed to
+    [B, H, S, D], so the gradient reaching the norm is a head-major view.  The backward takes it in
+    place through the strided entry point (no copy), and x's and the parameters' gradients match
+    the oracle on the logical rows."""
+    B, S, H, D = 2, 300, 32, 128
+    pdt = "bf16" if layer == "rmsnorm" else "f32"
+    wl = workloads.small(layer, B * S * H, D, "bf16", pdt, seed=9)
+    print("case:", wl, flush=True)
+    inp = workloads.make_inputs(wl)
+    calls = []
+    real = rwn._try_strided
+    monkeypatch.setattr(rwn, "_try_strided", lambda lib, fn, call: calls.append(fn) or real(lib, fn, call))
+    x = inp["x"].reshape(B, S, H, D).cuda().requires_grad_(True)
+    ps = [inp[k].cuda().requires_grad_(True) for k in {"dyt": ["alpha", "gamma", "beta"],
+                                                        "layernorm": ["gamma", "beta"], "rmsnorm": ["weight"]}[layer]]
+    if layer == "dyt":
+        y = ag.dyt(x, *ps)
+    elif layer == "layernorm":
+        y = ag.layer_norm(x, *ps, eps=wl.eps)
+    else:
+        y = ag.rms_norm(x, *ps, eps=wl.eps)
+    g = inp["dy"].reshape(B, S, H, D).transpose(1, 2).contiguous().cuda()   # upstream gradient of y.transpose(1, 2)
+    y.transpose(1, 2).backward(g)
+    torch.cuda.synchronize()
+    assert calls == [f"{'dyt' if layer == 'dyt' else layer}_bwd_strided"], calls
+    names = {"dyt": ["dalpha", "dgamma", "dbeta"], "layernorm": ["dgamma", "dbeta"], "rmsnorm": ["dweight"]}[layer]
+    got = {"y": y.detach().reshape(-1, D), "dx": x.grad.reshape(-1, D)}
+    got.update({nm: p.grad for p, nm in zip(ps, names)})
+    tol.assert_reports(gc.compare(layer, got, gc.oracle_run(layer, inp, wl.eps), gc.DT["bf16"], gc.DT[pdt]))
