@@ -11,9 +11,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "librwnorm.so")
 
-SOURCES = ["rwn_api.hip", "launch_common.hip", "launch_dyt.hip", "launch_layernorm.hip",
-           "launch_flat.hip", "launch_rmsnorm.hip", "launch_split.hip"]
-HEADERS = ["rwn_device.hpp", "rwn_kernels.hpp", "rwn_launch.hpp", "rwn_split.hpp"]
+SOURCES = ["rwn_api.hip", "launch_common.hip", "launch_dyt.hip", "launch_ln_fwd.hip", "launch_ln_bwd.hip",
+           "launch_flat.hip", "launch_rms_fwd.hip", "launch_rms_bwd.hip", "launch_split.hip",
+           "launch_strided_dyt.hip", "launch_strided_ln.hip", "launch_strided_rms.hip"]
+HEADERS = ["rwn_device.hpp", "rwn_kernels.hpp", "rwn_launch.hpp", "rwn_general.hpp", "rwn_split.hpp"]
 
 ARCH = os.environ.get("RWN_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -408,7 +408,6 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             p.pf = 1;
         else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
     }
-    if (layout) p.pf = 0;
     // Narrow aligned LayerNorm rows, one chunk and one row per thread, take the flat kernels
     // (plain loads on clamped row indices, no per-tile descriptors), which run fastest without
     // pipelining.

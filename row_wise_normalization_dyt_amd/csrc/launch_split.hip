@@ -78,20 +78,10 @@ hipError_t launch_ln_bwd_split(const Plan& p, int xdt, int pdt, const void* x, c
     });
 }
 
-// The RMSNorm form as a template value (0: Llama; 1: both float32 forms, with g.w_offset = 1 for
-// the (1 + weight) one).
-template <typename F>
-static hipError_t dispatch_split_variant(int variant, Geom& g, F&& f) {
-    g.w_offset = variant == RMS_ONE_PLUS_WEIGHT ? 1.0f : 0.0f;
-    if (variant == RMS_CAST_THEN_WEIGHT) return f(IC<0>{});
-    if (variant == RMS_WEIGHT_THEN_CAST || variant == RMS_ONE_PLUS_WEIGHT) return f(IC<1>{});
-    return hipErrorInvalidValue;
-}
-
 hipError_t launch_rms_fwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                                 float eps, void* y, float* rstd, hipStream_t s) {
     Geom g = make_geom(p);
-    return dispatch_split_variant(variant, g, [&](auto var) {
+    return dispatch_variant(variant, g, [&](auto var) {
         return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
             using T = typename decltype(tt)::type;
             using PT = typename decltype(pt)::type;
@@ -107,7 +97,7 @@ hipError_t launch_rms_fwd_split(const Plan& p, int xdt, int pdt, int variant, co
 hipError_t launch_rms_bwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
                                 const float* rstd, const void* w, float eps, void* dx, float* ws, hipStream_t s) {
     Geom g = make_geom(p);
-    return dispatch_split_variant(variant, g, [&](auto var) {
+    return dispatch_variant(variant, g, [&](auto var) {
         return dispatch_pg(ws, [&](auto pg) {
             return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
                 using T = typename decltype(tt)::type;

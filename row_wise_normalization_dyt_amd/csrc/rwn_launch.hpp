@@ -13,6 +13,9 @@ namespace rwn {
 
 enum Layer { LAYER_DYT = 0, LAYER_LN = 1, LAYER_RMS = 2 };
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+// RMSNorm forms: the Llama form rounds the normalized value to x's dtype before the weight
+// multiply; the two others multiply in float32 and round once, by weight or by (1 + weight).
+enum RmsVariant { RMS_CAST_THEN_WEIGHT = 0, RMS_WEIGHT_THEN_CAST = 1, RMS_ONE_PLUS_WEIGHT = 2 };
 
 // Supported (x dtype, parameter dtype) pairs: float32 x takes float32 parameters; a 16-bit x
 // takes float32 parameters or parameters of its own dtype.
@@ -57,7 +60,8 @@ struct Plan {
 // Plan for one call.  misalign_bytes: address of the [M, N] operands modulo 16 (a multiple of
 // the element size).  layout: 0 for dense [M, N] operands; 1 for strided operands whose rows
 // all start misalign_bytes past a 16-byte boundary; 2 for strided operands of any alignment
-// (SCALAR).  Strided plans run the general kernels with one row per thread, no pipelining.  cus: compute units of the device.  pdt: the parameter dtype, or -1 when
+// (SCALAR).  Strided plans run the general kernels with one row per thread.  cus: compute
+// units of the device.  pdt: the parameter dtype, or -1 when
 // the plan must hold for every parameter dtype of x's dtype (the workspace query).  occupancy:
 // ask the runtime how many workgroups of the chosen kernel fit on a CU (needs a current device;
 // false plans from launch bounds alone).  Returns false if N is too wide.
@@ -69,6 +73,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
 int resident_wgs_dyt(bool backward, const Plan& p, int xdt, int pdt);
 int resident_wgs_ln(bool backward, const Plan& p, int xdt, int pdt);
 int resident_wgs_rms(bool backward, const Plan& p, int xdt, int pdt);
+int resident_wgs_ln_bwd(const Plan& p, int xdt, int pdt);
+int resident_wgs_rms_bwd(const Plan& p, int xdt, int pdt);
+// Strided plans (layouts 1 and 2), launched from launch_strided_*.hip.
+int resident_wgs_dyt_strided(bool backward, const Plan& p, int xdt, int pdt);
+int resident_wgs_ln_strided(bool backward, const Plan& p, int xdt, int pdt);
+int resident_wgs_rms_strided(bool backward, const Plan& p, int xdt, int pdt);
 
 // hipOccupancyMaxActiveBlocksPerMultiprocessor for one kernel, cached (0 on failure).
 int kernel_occupancy(const void* kernel, int block, size_t dyn_lds);
@@ -124,6 +134,16 @@ hipError_t dispatch_ln_grads(const float* ws, int grads, F&& f) {
     }
 }
 
+// The form as a template value: 0 for the Llama form, 1 for both float32 forms (the
+// (1 + weight) one adds g.w_offset = 1 to the weight).
+template <typename F>
+hipError_t dispatch_variant(int variant, Geom& g, F&& f) {
+    g.w_offset = variant == RMS_ONE_PLUS_WEIGHT ? 1.0f : 0.0f;
+    if (variant == RMS_CAST_THEN_WEIGHT) return f(IC<0>{});
+    if (variant == RMS_WEIGHT_THEN_CAST || variant == RMS_ONE_PLUS_WEIGHT) return f(IC<1>{});
+    return hipErrorInvalidValue;
+}
+
 // Calls f(TypeTag<T>, TypeTag<PT>) for the supported dtype pairs.
 template <typename F>
 hipError_t dispatch_dtypes(int xdt, int pdt, F&& f) {
@@ -148,50 +168,59 @@ hipError_t dispatch_pf2(const Plan& p, F&& f) {
     return p.pf == 2 ? f(IC<2>{}) : p.pf ? f(IC<1>{}) : f(IC<0>{});
 }
 
-// Calls f(IC<MODE>, IC<CPT>, IC<RT>, IC<PF>, IC<LAY>) for the instantiated shapes.  Strided
-// plans (LAY 1: layouts 1 and 2) exist with one row per thread and no pipelining.
-template <typename T, typename F>
+// Calls f(IC<MODE>, IC<CPT>, IC<RT>, IC<PF>, IC<LAY>) for the instantiated shapes of one side:
+// S = false the dense plans (LAY 0), S = true the strided ones (LAY 1: layouts 1 and 2, one row
+// per thread).  A plan of the other side returns hipErrorInvalidValue.
+template <typename T, bool S, typename F>
 hipError_t dispatch_shape(const Plan& p, F&& f) {
     if ((p.pf && p.cpt * p.rt > 2) || (p.pf == 2 && (p.cpt * p.rt != 1 || p.mode == MODE_SCALAR)))
         return hipErrorInvalidValue;
-    if (p.layout) {
-        if (p.rt != 1 || p.pf != 0) return hipErrorInvalidValue;
+    if ((p.layout != 0) != S) return hipErrorInvalidValue;
+    if constexpr (S) {
+        if (p.rt != 1) return hipErrorInvalidValue;
+        const IC<1> strided;
         auto by_cpt = [&](auto mode) {
-            if (p.cpt == 1) return f(mode, IC<1>{}, IC<1>{}, IC<0>{}, IC<1>{});
-            if (p.cpt == 2) return f(mode, IC<2>{}, IC<1>{}, IC<0>{}, IC<1>{});
-            if (p.cpt == 4) return f(mode, IC<4>{}, IC<1>{}, IC<0>{}, IC<1>{});
+            if (p.cpt == 1) {
+                if constexpr (decltype(mode)::value == MODE_SCALAR)
+                    return dispatch_pf(p, [&](auto pf) { return f(mode, IC<1>{}, IC<1>{}, pf, strided); });
+                else
+                    return dispatch_pf2(p, [&](auto pf) { return f(mode, IC<1>{}, IC<1>{}, pf, strided); });
+            }
+            if (p.cpt == 2) return dispatch_pf(p, [&](auto pf) { return f(mode, IC<2>{}, IC<1>{}, pf, strided); });
+            if (p.cpt == 4) return f(mode, IC<4>{}, IC<1>{}, IC<0>{}, strided);
             return hipErrorInvalidValue;
         };
         if (p.mode == MODE_ALIGNED) return by_cpt(IC<MODE_ALIGNED>{});
         if (p.mode == MODE_SHIFTED) return by_cpt(IC<MODE_SHIFTED>{});
         return by_cpt(IC<MODE_SCALAR>{});
-    }
-    const IC<0> dense;
-    if (p.mode == MODE_ALIGNED) {
-        if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{}, IC<0>{}, dense);
-        if (p.rt == 2 && p.cpt == 1)
-            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{}, pf, dense); });
-        if (p.rt == 1) {
+    } else {
+        const IC<0> dense;
+        if (p.mode == MODE_ALIGNED) {
+            if (p.rt == 4 && p.cpt == 1) return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<4>{}, IC<0>{}, dense);
+            if (p.rt == 2 && p.cpt == 1)
+                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<2>{}, pf, dense); });
+            if (p.rt == 1) {
+                if (p.cpt == 1)
+                    return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf, dense); });
+                if (p.cpt == 2)
+                    return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{}, pf, dense); });
+                if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
+            }
+        } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
             if (p.cpt == 1)
-                return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<1>{}, IC<1>{}, pf, dense); });
+                return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf, dense); });
             if (p.cpt == 2)
-                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_ALIGNED>{}, IC<2>{}, IC<1>{}, pf, dense); });
-            if (p.cpt == 4) return f(IC<MODE_ALIGNED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
+                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{}, pf, dense); });
+            if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
+        } else if (p.mode == MODE_SCALAR && p.rt == 1) {
+            if (p.cpt == 1)
+                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{}, pf, dense); });
+            if (p.cpt == 2)
+                return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{}, pf, dense); });
+            if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
         }
-    } else if (p.mode == MODE_SHIFTED && p.rt == 1) {
-        if (p.cpt == 1)
-            return dispatch_pf2(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<1>{}, IC<1>{}, pf, dense); });
-        if (p.cpt == 2)
-            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SHIFTED>{}, IC<2>{}, IC<1>{}, pf, dense); });
-        if (p.cpt == 4) return f(IC<MODE_SHIFTED>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
-    } else if (p.mode == MODE_SCALAR && p.rt == 1) {
-        if (p.cpt == 1)
-            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<1>{}, IC<1>{}, pf, dense); });
-        if (p.cpt == 2)
-            return dispatch_pf(p, [&](auto pf) { return f(IC<MODE_SCALAR>{}, IC<2>{}, IC<1>{}, pf, dense); });
-        if (p.cpt == 4) return f(IC<MODE_SCALAR>{}, IC<4>{}, IC<1>{}, IC<0>{}, dense);
+        return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
 }
 
 // Largest workgroup each kernel shape is compiled for (its amdgpu_flat_work_group_size):
@@ -239,9 +268,6 @@ hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, co
                               const float* mean, const float* rstd, const void* gamma, float eps,
                               void* dx, float* ws, int grads, hipStream_t s);
 int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt);
-// RMSNorm forms: the Llama form rounds the normalized value to x's dtype before the weight
-// multiply; the two others multiply in float32 and round once, by weight or by (1 + weight).
-enum RmsVariant { RMS_CAST_THEN_WEIGHT = 0, RMS_WEIGHT_THEN_CAST = 1, RMS_ONE_PLUS_WEIGHT = 2 };
 
 hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                           float eps, void* y, float* rstd, hipStream_t s);
@@ -265,6 +291,19 @@ hipError_t launch_rms_fwd_split(const Plan& p, int xdt, int pdt, int variant, co
 hipError_t launch_rms_bwd_split(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
                                 const float* rstd, const void* w, float eps, void* dx, float* ws, hipStream_t s);
 int resident_wgs_split(int layer, bool backward, const Plan& p, int xdt, int pdt);
+hipError_t launch_dyt_fwd_strided(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                                  const void* gamma, const void* beta, void* y, hipStream_t s);
+hipError_t launch_dyt_bwd_strided(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                                  const void* alpha, const void* gamma, void* dx, float* ws, hipStream_t s);
+hipError_t launch_ln_fwd_strided(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
+                                 const void* beta, float eps, void* y, float* mean, float* rstd, hipStream_t s);
+hipError_t launch_ln_bwd_strided(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                                 const float* mean, const float* rstd, const void* gamma, float eps,
+                                 void* dx, float* ws, int grads, hipStream_t s);
+hipError_t launch_rms_fwd_strided(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
+                                  float eps, void* y, float* rstd, hipStream_t s);
+hipError_t launch_rms_bwd_strided(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* dy,
+                                  const float* rstd, const void* w, float eps, void* dx, float* ws, hipStream_t s);
 
 // Stage 2: sums the P partial rows of columns [c_lo, c_hi) (column c at ws + c * cs, partial
 // row p at + p * rs) into out0 (columns [0, N)), out1 ([N, 2N)) and out2 (column 2N, which also

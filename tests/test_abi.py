@@ -181,7 +181,7 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
 @pytest.mark.parametrize("layout", [1, 2])
 @pytest.mark.parametrize("backward", [False, True])
 def test_strided_plans(layout, backward):
-    """Strided operands take the general kernels with one row per thread and no pipelining;
+    """Strided operands take the general kernels with one row per thread;
     layout 2 (rows of mixed alignment) moves elements (SCALAR), and LayerNorm / RMSNorm take
     it up to 2048 16-bit or 4096 float32 elements, DyT at any width through column blocks."""
     for dtype, esz in ((torch.float32, 4), (torch.bfloat16, 2), (torch.float16, 2)):
@@ -200,7 +200,9 @@ def test_strided_plans(layout, backward):
                             rwn.plan(layer, backward, 4099, N, dtype, mis, cus=256, layout=layout)
                         continue
                     p = rwn.plan(layer, backward, 4099, N, dtype, mis, cus=256, layout=layout)
-                    assert p["rt"] == 1 and p["prefetch"] == 0 and p["flat"] == 0 and p["split"] == 0, p
+                    assert p["rt"] == 1 and p["flat"] == 0 and p["split"] == 0, p
+                    # pipelining only where a form exists: two tiles ahead for one vector chunk
+                    assert p["prefetch"] <= (2 if p["cpt"] == 1 and p["mode"] != 2 else 1 if p["cpt"] <= 2 else 0), p
                     if layout == 2:
                         assert p["mode"] == 2 and p["vec"] == 1, p
                     else:
