@@ -1,0 +1,103 @@
+"""Host logic of the binding's strided path (CPU only, no kernel runs): how torch views become the
+strided entry points' leading sizes and strides, when the strided path is taken, and the
+checks on caller-provided outputs and parameter vectors."""
+import pytest
+import torch
+
+import row_wise_normalization_dyt_amd as rwn
+
+
+def _layout(*ts):
+    out = rwn._row_layout(list(ts))
+    if out is None:
+        return None
+    n, lead, strides = out
+    return list(lead), [list(s) for s in strides]
+
+
+def test_contiguous_rows_merge_into_one_dimension():
+    x = torch.empty(4, 5, 6, 32)
+    assert _layout(x, torch.empty_like(x)) == ([120], [[32], [32]])
+
+
+def test_size_one_dimensions_are_dropped():
+    x = torch.empty(1, 7, 1, 3, 16)
+    assert _layout(x) == ([21], [[16]])
+    single = torch.empty(1, 1, 16)
+    assert _layout(single) == ([1], [[0]])
+
+
+def test_head_major_view_keeps_three_dimensions_with_each_tensors_strides():
+    B, S, H, D = 2, 300, 32, 128
+    hm = torch.empty(B, H, S, D).permute(0, 2, 1, 3)        # [B, S, H, D] view, head-major memory
+    dense = torch.empty(B, S, H, D)
+    lead, (s_hm, s_dense) = _layout(hm, dense)
+    assert lead == [B, S, H]
+    assert s_hm == [H * S * D, D, S * D]
+    assert s_dense == [S * H * D, H * D, D]
+    # the head-major view alone is a permuted dense tensor: its leading dimensions do not merge in
+    # logical order (rows are visited in [B, S, H] order, not in memory order)
+    assert _layout(hm)[0] == [B, S, H]
+
+
+def test_column_slice_has_one_row_stride():
+    big = torch.empty(100, 96)
+    assert _layout(big[:, 8:72], torch.empty(100, 64)) == ([100], [[96], [64]])
+
+
+def test_dimensions_merge_only_where_every_tensor_allows():
+    a = torch.empty(3, 4, 5, 8)                       # fully mergeable
+    b = torch.empty(3, 5, 4, 8).transpose(1, 2)       # dims 1, 2 swapped in memory
+    lead, (sa, sb) = _layout(a, b)
+    assert lead == [3, 4, 5]                          # b blocks every merge
+    assert sa == [160, 40, 8] and sb == [160, 8, 32]
+    c = torch.empty(3, 4, 6, 8)[:, :, :5]             # rows of 5 within blocks of 6
+    lead, (sa, sc) = _layout(a, c)
+    assert lead == [12, 5] and sa == [40, 8] and sc == [48, 8]
+
+
+def test_more_than_three_unmergeable_dimensions_fall_back():
+    x = torch.empty(2, 3, 5, 7, 16).permute(3, 1, 0, 2, 4)
+    assert rwn._row_layout([x]) is None
+
+
+def test_strided_path_is_taken_only_for_views_with_a_contiguous_last_dimension(monkeypatch):
+    monkeypatch.setattr(torch.Tensor, "is_cuda", property(lambda self: True))
+    dense = torch.empty(8, 64)
+    assert not rwn._use_strided([dense], [torch.empty(64)])
+    assert rwn._use_strided([dense[:, :32]], [None])                     # a column slice
+    assert rwn._use_strided([dense], [torch.empty(128)[::2]])            # a strided parameter
+    assert not rwn._use_strided([dense.t()], [None])                     # last dimension strided: copied
+    assert not rwn._use_strided([torch.empty(0, 64)], [None])            # no rows
+    x4 = torch.empty(2, 3, 4, 16)
+    dy4 = torch.empty(2, 4, 3, 16).transpose(1, 2)                      # a head-major gradient
+    assert rwn._use_strided([x4, dy4], [None]) and not rwn._use_strided([x4, x4], [None])
+
+
+def test_parameter_vectors_keep_their_stride():
+    v, s = rwn._svec(torch.arange(30.0)[::3], 10, "gamma", torch.device("cpu"))
+    assert s == 3 and v.data_ptr() == torch.arange(30.0)[::3].data_ptr() or v.stride(0) == 3
+    v, s = rwn._svec(torch.ones(1, 10), 10, "gamma", torch.device("cpu"))
+    assert s == 1 and v.shape == (10,)
+    assert rwn._svec(None, 10, "beta", torch.device("cpu")) == (None, 1)
+    with pytest.raises(ValueError, match="10 elements"):
+        rwn._svec(torch.ones(9), 10, "gamma", torch.device("cpu"))
+
+
+def test_fresh_outputs_share_the_inputs_phase_modulo_16_bytes():
+    base = torch.empty(1000, dtype=torch.bfloat16)
+    for off in range(8):
+        x = base[off:off + 640].view(10, 64)
+        y = rwn._fresh_rows(x)
+        assert y.shape == x.shape and y.is_contiguous()
+        assert y.data_ptr() % 16 == x.data_ptr() % 16
+
+
+def test_caller_outputs_are_checked():
+    x = torch.empty(10, 64)
+    with pytest.raises(ValueError, match="shape"):
+        rwn._out_strided(torch.empty(10, 32), x, "y")
+    with pytest.raises(ValueError, match="contiguous last dimension"):
+        rwn._out_strided(torch.empty(64, 10).t(), x, "y")
+    view = torch.empty(10, 96)[:, :64]
+    assert rwn._out_strided(view, x, "y") is view
