@@ -201,3 +201,62 @@ def test_strided_matches_dense_bitwise_where_plans_agree(strided_calls):
     assert torch.equal(y_s.view(torch.int16), y_d.view(torch.int16))
     assert torch.equal(r_s.view(torch.int32), r_d.view(torch.int32))
     assert torch.equal(dx_s.view(torch.int16), dx_d.view(torch.int16))
+
+
+@pytest.mark.parametrize("alpha", [float("inf"), 0.0])
+def test_strided_dyt_alpha_edges(alpha, strided_calls):
+    """DyT with alpha = +inf (tanh saturates, sech^2 = 0 taken as alpha * sech^2 = 0) and alpha = 0
+    on a column slice: the strided kernels keep the dense kernels' edge handling."""
+    M, N = 1031, 200
+    wl, inp = _inputs("dyt", M, N, "bf16", "f32", seed=21, alpha=alpha)
+
+    def sliced(t):
+        buf = torch.full((M, N + 24), float("nan"), dtype=t.dtype, device=DEV)
+        return buf, buf[:, 16:16 + N]
+
+    xv, _ = _embed(inp["x"].to(DEV), sliced)
+    dyv, _ = _embed(inp["dy"].to(DEV), sliced)
+    _check("dyt", "bf16", "f32", M, N, xv, dyv, _dev_params("dyt", inp), inp, wl, strided_calls)
+
+
+@pytest.mark.parametrize("layer", ["layernorm", "rmsnorm"])
+def test_strided_backward_recomputes_statistics(layer, strided_calls):
+    """Head-major x with the statistics not passed to the backward (recomputed from x there)."""
+    B, S, H, D = 2, 97, 8, 256
+    M = B * S * H
+    wl, inp = _inputs(layer, M, D, "bf16", "f32", seed=5)
+    x = inp["x"].reshape(B, S, H, D).to(DEV)
+    xv = torch.empty(B, H, S, D, dtype=x.dtype, device=DEV).permute(0, 2, 1, 3)
+    xv.copy_(x)
+    dy = inp["dy"].reshape(B, S, H, D).to(DEV)
+    strided_calls.clear()
+    if layer == "layernorm":
+        y, _, _ = rwn.layernorm_fwd(xv, inp["gamma"].to(DEV), inp["beta"].to(DEV), wl.eps, want_stats=False)
+        dx, dg, db = rwn.layernorm_bwd(xv, dy, None, None, inp["gamma"].to(DEV), wl.eps)
+        got = {"y": y, "dx": dx, "dgamma": dg, "dbeta": db}
+    else:
+        y, _ = rwn.rmsnorm_fwd(xv, inp["weight"].to(DEV), wl.eps, want_stats=False)
+        dx, dw = rwn.rmsnorm_bwd(xv, dy, None, inp["weight"].to(DEV), wl.eps)
+        got = {"y": y, "dx": dx, "dweight": dw}
+    torch.cuda.synchronize()
+    assert [fn for fn, ran in strided_calls if ran] == [f"{layer}_fwd_strided", f"{layer}_bwd_strided"]
+    got = {k: (v.reshape(M, D) if k in ("y", "dx") else v) for k, v in got.items()}
+    tol.assert_reports(gc.compare(layer, got, gc.oracle_run(layer, inp, wl.eps), gc.DT["bf16"], gc.DT["f32"]))
+
+
+def test_strided_layernorm_single_gradient(strided_calls):
+    """dgamma alone on a head-major x: the strided backward forms both gradients' partials and stage 2
+    reads only dgamma's columns, which are bitwise the full strided backward's; dx too."""
+    B, S, H, D = 2, 300, 32, 128
+    wl, inp = _inputs("layernorm", B * S * H, D, "bf16", "f32", seed=8)
+    xv = torch.empty(B, H, S, D, dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    xv.copy_(inp["x"].reshape(B, S, H, D).to(DEV))
+    dy = inp["dy"].reshape(B, S, H, D).to(DEV)
+    g = inp["gamma"].to(DEV)
+    _, mean, rstd = rwn.layernorm_fwd(xv, g, inp["beta"].to(DEV), wl.eps)
+    full = rwn.layernorm_bwd(xv, dy, mean, rstd, g, wl.eps)
+    one = rwn.layernorm_bwd(xv, dy, mean, rstd, g, wl.eps, need_dgamma=True, need_dbeta=False)
+    torch.cuda.synchronize()
+    assert one[2] is None
+    assert torch.equal(one[0].view(torch.int16), full[0].view(torch.int16))
+    assert torch.equal(one[1].view(torch.int32), full[1].view(torch.int32))
