@@ -196,7 +196,16 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     p.tpr = 64 * bw;
     p.rpp = std::max(1, kSplitBlock / p.tpr);
     p.ncb = 1;
-    p.pf = split_pf >= 0 ? split_pf : 0;
+    // Pipelined (one tile ahead) where it measured faster, at 65536 x N (us per launch, plain ->
+    // pipelined): 16-bit LayerNorm forwards of two or more waves per row (bf16 N = 2048 102.6 ->
+    // 89.1, 2049 105.3 -> 96.5, 4096 201.8 -> 182.4, 4097 206.0 -> 187.7) and 16-bit LayerNorm
+    // backwards of two chunks per lane (N = 2048 156.6 -> 134.4).  Elsewhere it measured slower
+    // or no faster: RMSNorm forwards (bf16 N = 4096 172.3 -> 181.5, 4097 191.9 -> 199.3),
+    // LayerNorm backwards of one chunk per lane (bf16 N = 2049 140.8 -> 166.5, 4097 285.6 ->
+    // 290.6), float32 LayerNorm (N = 1024 forward 85.2 -> 86.5).  Four chunks per lane stay plain:
+    // a second tile in flight would double their 32 elements of registers.
+    const bool pf_ln = layer == LAYER_LN && V == 8 && p.cpt == 2 && (backward || p.tpr >= 128);
+    p.pf = split_pf >= 0 ? split_pf : (pf_ln ? 1 : 0);
     p.flat = 0;
     const int ngrad = layer == LAYER_RMS ? 1 : 2;
     if (backward && p.rpp > 1 && (int64_t)ngrad * N * 4 > 48 * 1024) p.rpp = 1;
