@@ -202,7 +202,8 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     // backwards of two chunks per lane (N = 2048 156.6 -> 134.4).  Elsewhere it measured slower
     // or no faster: RMSNorm forwards (bf16 N = 4096 172.3 -> 181.5, 4097 191.9 -> 199.3),
     // LayerNorm backwards of one chunk per lane (bf16 N = 2049 140.8 -> 166.5, 4097 285.6 ->
-    // 290.6), float32 LayerNorm (N = 1024 forward 85.2 -> 86.5).  Four chunks per lane stay plain:
+    // 290.6), DyT (bf16 N = 2048 backward 166.2 -> 187.0, 4096 342.9 -> 367.3), float32 LayerNorm
+    // (N = 1024 forward 85.2 -> 86.5).  Four chunks per lane stay plain:
     // a second tile in flight would double their 32 elements of registers.
     const bool pf_ln = layer == LAYER_LN && V == 8 && p.cpt == 2 && (backward || p.tpr >= 128);
     p.pf = split_pf >= 0 ? split_pf : (pf_ln ? 1 : 0);
@@ -231,6 +232,53 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     return true;
 }
 
+static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pdt);
+
+// Flat LayerNorm plan with 12-byte lane chunks (rwn_kernels.hpp) for rows of 12 * 2^k bytes,
+// 2^k <= 64 lanes, on 4-byte aligned operands.  Such rows in 16-byte chunks leave a quarter of
+// their lanes idle, or are not whole chunks at all.  Measured at LayerNorm 401408 x 24 float32
+// on one MI355X against the 16-byte flat kernels: forward 16.3 -> 15.4 us, backward stage 1
+// 21.1 -> 20.5 us.  Four waves per workgroup (fewer for small M); tiles are the waves' row
+// groups (the forward's two steps of them), dealt round-robin over a persistent grid.
+static bool plan_flat12(bool backward, int64_t M, int64_t N, int xdt, int pdt, int cus, bool occupancy,
+                        int wg_per_cu, int min_waves, Plan* pp) {
+    const int esz = xdt == DT_F32 ? 4 : 2;
+    if ((N * esz) % 12) return false;
+    const int64_t lanes = N * esz / 12;
+    if (lanes > 64 || (lanes & (lanes - 1))) return false;
+    Plan& p = *pp;
+    p.mode = MODE_ALIGNED;
+    p.flat = 2;
+    p.split = 0;
+    p.cpt = 1;
+    p.tpr = (int)lanes;
+    p.rt = backward || lanes == 1 ? 1 : 2;
+    p.ncb = 1;
+    p.pf = 0;
+    p.kt = 0;
+    const int64_t rows_per_wave = (64 / p.tpr) * p.rt;
+    const int64_t waves = std::min<int64_t>(4, (M + rows_per_wave - 1) / rows_per_wave);
+    p.block = (int)(64 * std::max<int64_t>(1, waves));
+    p.rpp = p.block / p.tpr;
+    p.ntiles = (M + (int64_t)p.rpp * p.rt - 1) / ((int64_t)p.rpp * p.rt);
+    p.lds_bytes = backward ? (size_t)2 * (12 / esz) * p.block * sizeof(float) : 0;
+    int64_t occ = 0;
+    if (occupancy) {
+        const int pdts[3] = {DT_F32, DT_BF16, DT_F16};
+        for (int i = 0; i < 3; ++i) {
+            if (pdt >= 0 && pdts[i] != pdt) continue;
+            if (!dtype_pair_ok(xdt, pdts[i])) continue;
+            const int n = resident_wgs(LAYER_LN, backward, p, xdt, pdts[i]);
+            if (n > 0) occ = occ == 0 ? n : std::min<int64_t>(occ, n);
+        }
+    }
+    p.strided = 1;
+    persistent_grid(p, cus, occ, wg_per_cu, min_waves);
+    p.xcd_remap = 0;   // narrow rows stream faster in the hardware's workgroup order
+    if (backward) partial_layout(LAYER_LN, p);
+    return true;
+}
+
 static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pdt) {
     if (layer == LAYER_DYT) return resident_wgs_dyt(backward, p, xdt, pdt);
     if (layer == LAYER_LN) return resident_wgs_ln(backward, p, xdt, pdt);
@@ -251,6 +299,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int packed_rows = env_int("RWN_PACKED_ROWS", 0, 1, 1);
     static const int flat_rows = env_int("RWN_FLAT", 0, 1, 1);
     static const int split_rows = env_int("RWN_SPLIT", 0, 2, 1);
+    static const int flat12_rows = env_int("RWN_FLAT12", 0, 1, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -276,6 +325,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             p.mode = MODE_SCALAR;
             chunks = N;
         }
+    }
+    if (flat_rows && flat12_rows && layer == LAYER_LN && layout == 0 && prefetch < 0 && blocked_k == 0 &&
+        misalign_bytes % 4 == 0 &&
+        plan_flat12(backward, M, N, xdt, pdt, cus, occupancy, wg_per_cu, min_waves, &p)) {
+        *out = p;
+        return true;
     }
     // Split-row kernels: every wide row not aligned to 16-byte chunks, and aligned wide rows of at
     // most max_w waves per row slot.  Measured against the general kernels (65536 x N bf16, forward

@@ -1,5 +1,6 @@
-// Launchers of the flat LayerNorm kernels (narrow aligned rows): every dtype pair, group size
-// 1..64 lanes, with and without parameter-gradient partials and given statistics.
+// Launchers of the flat LayerNorm kernels (narrow rows; p.flat 1: 16-byte chunks on aligned rows,
+// 2: 12-byte chunks): every dtype pair, group size 1..64 lanes, with and without
+// parameter-gradient partials and given statistics.
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -20,6 +21,11 @@ static hipError_t dispatch_tpr(const Plan& p, F&& f) {
     }
 }
 
+// The 12-byte forward's steps per tile: two, or one for single-lane rows (a wave's tile of 64
+// rows already fills its lanes' statistics store).
+template <int TPR>
+constexpr int flat12_rt() { return TPR == 1 ? 1 : 2; }
+
 hipError_t launch_ln_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* gamma,
                               const void* beta, float eps, void* y, float* mean, float* rstd,
                               hipStream_t s) {
@@ -29,7 +35,14 @@ hipError_t launch_ln_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, co
         using T = typename decltype(tt)::type;
         using PT = typename decltype(pt)::type;
         return dispatch_tpr(p, [&](auto tpr) {
-            return launch(ln_fwd_flat_kernel<T, PT, decltype(tpr)::value>, dim3((unsigned)p.grid),
+            constexpr int R = decltype(tpr)::value;
+            if (p.flat == 2) {
+                if (p.rt != flat12_rt<R>() || p.block % 64) return hipErrorInvalidValue;
+                return launch(ln_fwd_flat12_kernel<T, PT, R, flat12_rt<R>()>, dim3((unsigned)p.grid),
+                              dim3(p.block), 0, s, (const T*)x, (const PT*)gamma, (const PT*)beta, eps,
+                              (T*)y, mean, rstd, g);
+            }
+            return launch(ln_fwd_flat_kernel<T, PT, R>, dim3((unsigned)p.grid),
                           dim3(p.block), 0, s, (const T*)x, (const PT*)gamma, (const PT*)beta, eps,
                           (T*)y, mean, rstd, g);
         });
@@ -48,6 +61,12 @@ hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, co
             using PT = typename decltype(pt)::type;
             return dispatch_tpr(p, [&](auto tpr) {
                 constexpr int R = decltype(tpr)::value, G = decltype(pg)::value;
+                if (p.flat == 2) {
+                    if (p.rt != 1 || p.block % 64) return hipErrorInvalidValue;
+                    auto k = st ? ln_bwd_flat12_kernel<T, PT, R, G, 1> : ln_bwd_flat12_kernel<T, PT, R, G, 0>;
+                    return launch(k, dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
+                                  (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
+                }
                 auto k = st ? ln_bwd_flat_kernel<T, PT, R, G, 1> : ln_bwd_flat_kernel<T, PT, R, G, 0>;
                 return launch(k, dim3((unsigned)p.grid), dim3(p.block), p.lds_bytes, s, (const T*)x,
                               (const T*)dy, mean, rstd, (const PT*)gamma, eps, (T*)dx, ws, g);
@@ -63,8 +82,13 @@ int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt) {
         using PT = typename decltype(pt)::type;
         return dispatch_tpr(p, [&](auto tpr) {
             constexpr int R = decltype(tpr)::value;
-            const void* k = backward ? (const void*)ln_bwd_flat_kernel<T, PT, R, 3, 1>
-                                     : (const void*)ln_fwd_flat_kernel<T, PT, R>;
+            const void* k;
+            if (p.flat == 2)
+                k = backward ? (const void*)ln_bwd_flat12_kernel<T, PT, R, 3, 1>
+                             : (const void*)ln_fwd_flat12_kernel<T, PT, R, flat12_rt<R>()>;
+            else
+                k = backward ? (const void*)ln_bwd_flat_kernel<T, PT, R, 3, 1>
+                             : (const void*)ln_fwd_flat_kernel<T, PT, R>;
             n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
             return hipSuccess;
         });

@@ -857,7 +857,7 @@ RWN_API rwn_status rwn_plan(int layer, int backward, int64_t M, int64_t N, rwn_d
         return fail(RWN_ERR_UNSUPPORTED, "%s: no launch plan for N = %lld", fn, (long long)N);
     out[0] = p.mode; out[1] = p.cpt; out[2] = p.rt; out[3] = p.tpr; out[4] = p.rpp;
     out[5] = p.block; out[6] = p.grid; out[7] = p.ntiles;
-    out[8] = p.mode == MODE_SCALAR ? 1 : 16 / esz;
+    out[8] = p.flat == 2 ? 12 / esz : p.mode == MODE_SCALAR ? 1 : 16 / esz;
     out[9] = p.strided ? 0 : p.kt;
     out[10] = p.strided;
     out[11] = p.ncb;

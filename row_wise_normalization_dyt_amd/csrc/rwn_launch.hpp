@@ -40,7 +40,8 @@ struct Plan {
     int strided = 0;          // 1: grid-stride over tiles (grid * rpp a multiple of V)
     int ncb = 1;              // DyT column blocks per row (grid a multiple of ncb)
     int xcd_remap = 0;        // renumber workgroups XCD-contiguously (needs grid % 8 == 0)
-    int flat = 0;             // LayerNorm narrow aligned rows through the flat kernels
+    int flat = 0;             // LayerNorm narrow rows through the flat kernels: 1 with 16-byte
+                              // chunks (aligned rows), 2 with 12-byte chunks (12 * 2^k-byte rows)
     int split = 0;            // wide unaligned rows through the split-row kernels (rwn_split.hpp)
     int pf = 0;               // software-pipelined tile loop: 0 off, 1 one tile ahead (cpt * rt <= 2),
                               // 2 two tiles ahead (cpt * rt == 1, vector modes)

@@ -115,7 +115,8 @@ def test_trace_and_probe_argument_errors(lib):
 
 SHAPES = [(1, 1), (7, 24), (4096, 64), (401408, 24), (1048573, 32), (1048573, 128), (1048573, 256),
           (16384, 2048), (8192, 4096), (65536, 1025), (65536, 4096), (65536, 8192), (65536, 16384),
-          (3, 7), (257, 17), (7, 129), (4099, 130), (7, 2049), (65537, 255), (5, 1023)]
+          (3, 7), (257, 17), (7, 129), (4099, 130), (7, 2049), (65537, 255), (5, 1023),
+          (9, 3), (1000, 6), (1001, 48), (33, 192), (65, 384)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
@@ -143,6 +144,18 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
                 assert p["ntiles"] * p["rpp"] >= M > (p["ntiles"] - 1) * p["rpp"]
                 gt = p["grid"]
                 assert 1 <= gt <= max(p["ntiles"], 1) and (gt >= p["ntiles"] or (gt * p["rpp"]) % V == 0), p
+                continue
+            if p["flat"] == 2:
+                # LayerNorm rows of 12 * 2^k bytes in 12-byte chunks: every lane of a row's
+                # power-of-two group live, 4-byte aligned operands, whole waves, a persistent grid
+                assert layer == "layernorm" and mis % 4 == 0 and V == 12 // esz, p
+                assert N * esz == 12 * p["tpr"] and p["tpr"] <= 64 and p["tpr"] & (p["tpr"] - 1) == 0, p
+                assert p["cpt"] == 1 and p["ncb"] == 1 and p["prefetch"] == 0 and p["xcd_remap"] == 0, p
+                assert p["rt"] == (1 if backward or p["tpr"] == 1 else 2), p
+                assert p["block"] % 64 == 0 and 64 <= p["block"] <= 256 and p["rpp"] * p["tpr"] == p["block"], p
+                rows_per_tile = p["rpp"] * p["rt"]
+                assert p["ntiles"] * rows_per_tile >= M > (p["ntiles"] - 1) * rows_per_tile, p
+                assert p["strided"] == 1 and 1 <= p["grid"] <= p["ntiles"], p
                 continue
             # chunks of a row: worst shift is V-1 elements in the shifted mode
             chunks = -(-(N + (V - 1 if p["mode"] == 1 else 0)) // V)
@@ -272,22 +285,30 @@ def test_plan_uses_narrow_tiles_for_narrow_rows():
 
 @pytest.mark.parametrize("backward", [False, True])
 def test_flat_plans(backward):
-    """The flat kernels take exactly the narrow aligned LayerNorm plans with one chunk and one
-    row per thread (group sizes 1..64 lanes, no pipelining, at most 256 threads); every other
-    plan, and every other layer, keeps the general kernels."""
+    """LayerNorm rows of 12 * 2^k bytes (2^k <= 64) on 4-byte aligned operands take the flat
+    kernels with 12-byte chunks (flat 2); other narrow aligned LayerNorm plans with one chunk and
+    one row per thread (group sizes 1..64 lanes, no pipelining, at most 256 threads) take the
+    16-byte flat kernels (flat 1); every other plan, and every other layer, keeps the general
+    kernels."""
     for dtype, V in ((torch.float32, 4), (torch.bfloat16, 8), (torch.float16, 8)):
-        for N in (V, 2 * V, 24 if V == 4 else 32, 16 * V, 64 * V, 64 * V + V, 1025):
-            for mis in (0, 2 if V == 8 else 4):
+        esz = 16 // V
+        for N in (V, 2 * V, 24 if V == 4 else 32, 24, 3 * V, 6 * V, 48 * V, 16 * V, 64 * V, 64 * V + V, 1025):
+            for mis in (0, 2 if V == 8 else 4, 4 if V == 8 else 8):
                 for layer in ("dyt", "layernorm", "rmsnorm"):
                     p = rwn.plan(layer, backward, 4099, N, dtype, misalign_bytes=mis, cus=256)
+                    lanes = N * esz // 12
+                    want12 = (layer == "layernorm" and (N * esz) % 12 == 0 and lanes <= 64
+                              and lanes & (lanes - 1) == 0 and mis % 4 == 0)
                     want = (layer == "layernorm" and p["mode"] == 0 and p["cpt"] == 1 and p["rt"] == 1
                             and p["tpr"] <= 64 and p["ncb"] == 1)
-                    assert p["flat"] == int(want), (layer, N, mis, p)
-                    if p["flat"]:
+                    assert p["flat"] == (2 if want12 else int(want)), (layer, N, mis, p)
+                    if p["flat"] == 1:
                         assert N % V == 0 and mis == 0 and p["prefetch"] == 0 and p["block"] <= 256, p
                         assert p["tpr"] in (1, 2, 4, 8, 16, 32, 64) and p["block"] == p["tpr"] * p["rpp"], p
+                    if p["flat"] == 2:
+                        assert p["tpr"] == lanes and p["vec"] == 12 // esz and p["prefetch"] == 0, p
     p = rwn.plan("layernorm", backward, 401408, 24, torch.float32, cus=256)
-    assert p["flat"] == 1 and p["xcd_remap"] == 0
+    assert p["flat"] == 2 and p["xcd_remap"] == 0 and p["tpr"] == 8
 
 
 def test_plan_is_deterministic():

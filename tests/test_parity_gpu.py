@@ -275,7 +275,7 @@ def test_dx_only_backward_matches_full_backward(layer):
 
 LN_GRAD_SHAPES = [(4099, 24, "f32", "f32"), (1031, 128, "bf16", "f32"), (263, 1024, "bf16", "bf16"),
                   (257, 1025, "bf16", "f32"), (65, 17, "f16", "f16"), (67, 4096, "f32", "f32"),
-                  (129, 3001, "f16", "f32"), (401408, 24, "f32", "f32")]
+                  (129, 3001, "f16", "f32"), (401408, 24, "f32", "f32"), (1031, 48, "bf16", "f32")]
 
 
 @pytest.mark.parametrize("which", ["dgamma", "dbeta"])
@@ -394,7 +394,7 @@ print("BAD", bad, flush=True)
 @pytest.mark.parametrize("env", ["RWN_PREFETCH=0", "RWN_PREFETCH=1", "RWN_PREFETCH=2", "RWN_FWD_RT=4 RWN_BWD_RT=2",
                                  "RWN_WIDE_CPT=4", "RWN_BLOCKED_K=3", "RWN_XCD_REMAP=0 RWN_WG_PER_CU=2",
                                  "RWN_FLAT=0", "RWN_XCD_REMAP=1 RWN_BLOCKED_K=2", "RWN_SPLIT=0", "RWN_SPLIT=2",
-                                 "RWN_SPLIT_CPT=1", "RWN_SPLIT_CPT=4"])
+                                 "RWN_SPLIT_CPT=1", "RWN_SPLIT_CPT=4", "RWN_FLAT12=0"])
 def test_tuning_overrides_keep_parity(env):
     """The tuning knobs change the launch plan (pipelining depth, rows per thread, chunks per
     thread, tile assignment, grid); every plan they reach must still match the oracle.  The
