@@ -339,10 +339,14 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // 191.1 (DyT), DyT backward 315.2 -> 306.8; 16384 x 2048 RMSNorm 27.2 / 45.8 -> 25.4 / 44.6.
     // LayerNorm / RMSNorm backwards of four or more waves per row ran slower split (65536 x 4096:
     // 288.2 -> 332.0, 271.5 -> 284.3 us), and forwards of eight no faster (N = 8192).
+    // RMSNorm backwards of 4-wave rows split as well when the rows are few per CU (at most 64):
+    // 8192 x 4096 bf16 stage 1 43.2 -> 41.1 us, while at 65536 x 4096 the split form measured
+    // 268.2 -> 273.0 us.
+    const bool few_rows = M <= (int64_t)64 * cus;
     int split_max_w = 0;
     if (p.mode == MODE_SHIFTED) split_max_w = 8;
     else if (p.mode == MODE_ALIGNED && chunks > 64)
-        split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT) ? 4 : 2;
+        split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
     if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
         plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, xcd_remap,
                    split_max_w, &p)) {
