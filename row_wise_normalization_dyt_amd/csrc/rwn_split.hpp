@@ -115,10 +115,29 @@ __device__ __forceinline__ void split_load(const T* __restrict__ p, int64_t e0, 
     r.s = ins ? bits : 0u;
 }
 
-template <typename T, int CPT>
+// Discard target of the chunk stores with SINK set: 16 bytes per wave of 64 workgroup numbers.
+// Nothing reads it; concurrent kernels may write it at will.
+static __device__ __align__(256) u32x4 split_sink[64 * (kSplitBlock / 64)];
+
+// Store of main chunk k.  Without SINK a lane whose chunk does not exist (or whose row is past
+// M) skips the store behind a branch; with SINK it stores to split_sink instead, so the store
+// is issued on every path.  The compiler can then count the memory operations in flight exactly
+// (a store that may or may not have been issued makes it wait for all of them) and schedule the
+// arithmetic around the stores.  Measured per kernel, SINK is set where it was faster: DyT
+// backwards of two chunks per lane (65536 x N bf16 stage 1: N = 1025 92.7 -> 84.6 us, 4096
+// 323.0 -> 292.5) and pipelined LayerNorm backwards of two chunks per lane (N = 2048 135.6 ->
+// 130.8); one-chunk LayerNorm / RMSNorm backwards ran far slower with it (N = 1025: 73.8 -> 108.4
+// and 70.8 -> 95.1) and forwards no faster.
+template <typename T, int CPT, bool SINK = false>
 __device__ __forceinline__ void split_store_chunk(T* __restrict__ p, int64_t e0, const SplitCtx<T, CPT>& m, int k,
                                                   const float* o, bool rv) {
-    if (rv && m.ok[k]) __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(p + e0 + m.col[k]));
+    if constexpr (SINK) {
+        u32x4* dst = (rv && m.ok[k]) ? reinterpret_cast<u32x4*>(p + e0 + m.col[k])
+                                     : split_sink + ((blockIdx.x & 63) * (kSplitBlock / 64) + (threadIdx.x >> 6));
+        __builtin_nontemporal_store(pack_chunk<T>(o), dst);
+    } else {
+        if (rv && m.ok[k]) __builtin_nontemporal_store(pack_chunk<T>(o), reinterpret_cast<u32x4*>(p + e0 + m.col[k]));
+    }
 }
 
 template <typename T, int CPT>
@@ -298,7 +317,7 @@ dyt_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT
                 for (int v = 0; v < V; ++v)
                     o[v] = elem(fin, in.xr.get(k, v), in.gr.get(k, v), ga[k * V + v], live, acc[0][k * V + v],
                                 acc[1][k * V + v]);
-                split_store_chunk<T, CPT>(dx, in.at.e0, c, k, o, rv);
+                split_store_chunk<T, CPT, CPT == 2>(dx, in.at.e0, c, k, o, rv);
             }
             const float os = elem(fin, in.xr.gets(), in.gr.gets(), gs, rv && c.sok, accs[0], accs[1]);
             split_store_scalar<T, CPT>(dx, in.at.e0, c, os, rv);
@@ -462,7 +481,7 @@ ln_bwd_split_kernel(const T* __restrict__ x, const T* __restrict__ dy, const flo
                 if constexpr (PG & 2) acc[IB][e] += gv;
                 o[v] = rs * (gv * ga[e] - c1 - xh * c2);
             }
-            split_store_chunk<T, CPT>(dx, in.at.e0, c, k, o, rv);
+            split_store_chunk<T, CPT, CPT == 2 && PF == 1>(dx, in.at.e0, c, k, o, rv);
         }
         {
             const float gv = in.gr.gets();
