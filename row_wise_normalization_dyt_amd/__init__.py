@@ -33,14 +33,25 @@ def _dt(t: torch.Tensor, name: str) -> int:
     return _DT[t.dtype]
 
 
-def _as_2d(x: torch.Tensor, name: str) -> torch.Tensor:
+def _rows12(N: int, esz: int) -> bool:
+    """LayerNorm rows of 12 * 2^k bytes (2^k <= 64 lanes): the library moves them in 12-byte
+    chunks, which need only 4-byte alignment."""
+    b = N * esz
+    lanes = b // 12
+    return b % 12 == 0 and 1 <= lanes <= 64 and lanes & (lanes - 1) == 0
+
+
+def _as_2d(x: torch.Tensor, name: str, rows12: bool = False) -> torch.Tensor:
+    """x as a contiguous [M, N] matrix.  rows12: the caller's rows are LayerNorm rows the
+    library takes in 12-byte chunks, so a view 4, 8 or 12 bytes past a 16-byte boundary is kept."""
     if not x.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if x.dim() < 1:
         raise ValueError(f"{name} must have at least one dimension")
     x = x.contiguous()
     x = x.reshape(-1, x.shape[-1]) if x.dim() != 2 else x
-    if x.data_ptr() % 16 and x.shape[-1] % (16 // x.element_size()) == 0:
+    keep = rows12 and x.data_ptr() % 4 == 0 and _rows12(x.shape[-1], x.element_size())
+    if x.data_ptr() % 16 and x.shape[-1] % (16 // x.element_size()) == 0 and not keep:
         # Rows of a misaligned view would straddle chunk boundaries; an aligned copy takes the
         # faster aligned kernels.
         x = x.clone()
@@ -333,7 +344,7 @@ def layernorm_fwd(x: torch.Tensor, gamma: Optional[torch.Tensor], beta: Optional
                         n, lead, N, _ptr(xs), sx, _dt(xs, "x"), _ptr(g), gs, _ptr(b), bs, pd, float(eps), _ptr(ys),
                         sy, _ptr(mu), _ptr(rs), _stream(xs.device))):
                     return ys, mu, rs
-    x2 = _as_2d(x, "x")
+    x2 = _as_2d(x, "x", rows12=True)
     M, N = x2.shape
     gamma, beta = _vec(gamma, N, "gamma", x2.device), _vec(beta, N, "beta", x2.device)
     pdt = _param_dtype(gamma, beta) if (gamma is not None or beta is not None) else _lib.RWN_F32
@@ -386,7 +397,7 @@ def layernorm_bwd(x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor
                         _DT[pdtype], float(eps), _ptr(dxs), sdx, _ptr(dg), _ptr(db), _ptr(ws), _ws_bytes(ws),
                         _stream(xs.device))):
                     return dxs, dg, db
-    x2, dy2 = _as_2d(x, "x"), _as_2d(dy, "dy")
+    x2, dy2 = _as_2d(x, "x", rows12=True), _as_2d(dy, "dy", rows12=True)
     x2, dy2 = _pair(x2, dy2)
     M, N = x2.shape
     gamma = _vec(gamma, N, "gamma", x2.device)

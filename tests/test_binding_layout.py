@@ -102,3 +102,29 @@ def test_caller_outputs_are_checked():
         rwn._out_strided(torch.empty(64, 10).t(), x, "y")
     view = torch.empty(10, 96)[:, :64]
     assert rwn._out_strided(view, x, "y") is view
+
+
+def test_rows12_rule_matches_the_planner():
+    """The binding keeps a 4-byte-aligned LayerNorm view exactly where the planner takes the
+    12-byte flat kernels for it (every width up to 400, both element sizes)."""
+    for dtype in (torch.float32, torch.bfloat16):
+        esz = 4 if dtype == torch.float32 else 2
+        for N in range(1, 401):
+            p = rwn.plan("layernorm", False, 1000, N, dtype, misalign_bytes=4, cus=256)
+            assert rwn._rows12(N, esz) == (p["flat"] == 2), (dtype, N, p)
+
+
+def test_layernorm_rows12_views_are_not_copied(monkeypatch):
+    monkeypatch.setattr(torch.Tensor, "is_cuda", property(lambda self: True))
+    buf = torch.empty(8 + 100 * 24, dtype=torch.float32)
+    base = (16 - buf.data_ptr() % 16) // 4           # element index of a 16-byte boundary
+    view = buf[base + 1:base + 1 + 100 * 24].view(100, 24)   # 4 bytes past it
+    assert view.data_ptr() % 16 == 4
+    assert rwn._as_2d(view, "x", rows12=True).data_ptr() == view.data_ptr()   # taken as it is
+    assert rwn._as_2d(view, "x").data_ptr() % 16 == 0                         # other layers: aligned copy
+    b16 = torch.empty(16 + 100 * 48, dtype=torch.bfloat16)
+    base = (16 - b16.data_ptr() % 16) // 2
+    odd = b16[base + 1:base + 1 + 100 * 48].view(100, 48)                      # 2 bytes past: not 4-aligned
+    assert rwn._as_2d(odd, "x", rows12=True).data_ptr() % 16 == 0
+    even = b16[base + 2:base + 2 + 100 * 48].view(100, 48)                     # 4 bytes past
+    assert rwn._as_2d(even, "x", rows12=True).data_ptr() == even.data_ptr()

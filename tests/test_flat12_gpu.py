@@ -169,3 +169,33 @@ def test_gradient_subsets(which):
                 assert torch.equal(one[k].view(torch.uint8), full[k].view(torch.uint8)), (wl.name, name)
             else:
                 assert one[k] is None, (wl.name, name)
+
+
+@pytest.mark.parametrize("xdt,offset_bytes", [("f32", 4), ("bf16", 12)])
+def test_binding_keeps_four_byte_aligned_views(xdt, offset_bytes):
+    """Through the Python binding: x and dy views offset_bytes past a 16-byte boundary are
+    passed as they are (no aligned copy), y and dx come back at the same offset, and every
+    result matches the oracle."""
+    esz = 4 if xdt == "f32" else 2
+    off = offset_bytes // esz
+    reps = []
+    for lanes, M in ((8, 1031), (64, 77)):
+        N = 12 * lanes // esz
+        wl = workloads.small("layernorm", M, N, xdt, "f32", seed=M + N)
+        _banner(wl, "binding, offset bytes", offset_bytes)
+        inp = workloads.make_inputs(wl)
+        dev = {}
+        for k, v in inp.items():
+            if k in ("x", "dy"):
+                buf = torch.empty(v.numel() + 16, dtype=v.dtype, device=DEV)
+                view = buf[off:off + v.numel()].view(v.shape)
+                view.copy_(v.to(DEV))
+                assert view.data_ptr() % 16 == offset_bytes
+                dev[k] = view
+            else:
+                dev[k] = v.to(DEV)
+        g = gc.gpu_run("layernorm", dev, wl.eps, poison=False)
+        assert g["y"].data_ptr() % 16 == offset_bytes and g["dx"].data_ptr() % 16 == offset_bytes
+        o = gc.oracle_run("layernorm", inp, wl.eps)
+        reps += gc.compare("layernorm", g, o, gc.DT[xdt], torch.float32)
+    tol.assert_reports(reps)
