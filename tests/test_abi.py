@@ -334,7 +334,7 @@ for layer in ("dyt", "layernorm", "rmsnorm"):
                     cap = 256 if p["rt"] > 1 else (512 if p["cpt"] == 1 or (p["cpt"] == 4 and esz == 2) else 1024)
                     if p["block"] > cap or p["block"] < p["tpr"] * p["rpp"] or p["block"] % 64:
                         bad.append((layer, str(dt), N, mis, bwd, p))
-                    if p["prefetch"] and p["cpt"] * p["rt"] > 2:     # no pipelined form
+                    if p["prefetch"] and p["cpt"] * p["rt"] > 2 and not p["split"]:   # no pipelined form
                         bad.append(("prefetch", layer, str(dt), N, mis, bwd, p))
                     if p["strided"] and p["grid"] * ((p["block"] + 63) // 64) > 32 * 256:
                         bad.append(("waves", layer, str(dt), N, mis, bwd, p))
@@ -347,7 +347,8 @@ print("BAD", bad)
 
 @pytest.mark.parametrize("env", ["RWN_WIDE_BLOCK=1024", "RWN_WIDE_BLOCK=64", "RWN_FWD_RT=4", "RWN_BWD_RT=2",
                                  "RWN_MIN_WAVES=32", "RWN_WG_PER_CU=3", "RWN_BLOCKED_K=3", "RWN_PREFETCH=1",
-                                 "RWN_PREFETCH=0", "RWN_X=0", "RWN_FLAT=0"])
+                                 "RWN_PREFETCH=0", "RWN_X=0", "RWN_FLAT=0", "RWN_FLAT12=0", "RWN_SPLIT_PF=1",
+                                 "RWN_SPLIT_PF=0", "RWN_PACKED_ROWS=0", "RWN_SPLIT=2", "RWN_SPLIT_CPT=4"])
 def test_plans_respect_kernel_launch_bounds_under_tuning_overrides(env):
     """Every plan's workgroup fits the launch bound its kernel was compiled for, also with the
     tuning overrides set (a plan over the bound would fail to launch)."""

@@ -394,7 +394,8 @@ print("BAD", bad, flush=True)
 @pytest.mark.parametrize("env", ["RWN_PREFETCH=0", "RWN_PREFETCH=1", "RWN_PREFETCH=2", "RWN_FWD_RT=4 RWN_BWD_RT=2",
                                  "RWN_WIDE_CPT=4", "RWN_BLOCKED_K=3", "RWN_XCD_REMAP=0 RWN_WG_PER_CU=2",
                                  "RWN_FLAT=0", "RWN_XCD_REMAP=1 RWN_BLOCKED_K=2", "RWN_SPLIT=0", "RWN_SPLIT=2",
-                                 "RWN_SPLIT_CPT=1", "RWN_SPLIT_CPT=4", "RWN_FLAT12=0"])
+                                 "RWN_SPLIT_CPT=1", "RWN_SPLIT_CPT=4", "RWN_FLAT12=0", "RWN_SPLIT_PF=0",
+                                 "RWN_SPLIT_PF=1", "RWN_MIN_WAVES=32", "RWN_WIDE_BLOCK=1024", "RWN_PACKED_ROWS=0"])
 def test_tuning_overrides_keep_parity(env):
     """The tuning knobs change the launch plan (pipelining depth, rows per thread, chunks per
     thread, tile assignment, grid); every plan they reach must still match the oracle.  The
