@@ -236,10 +236,11 @@ static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pd
 
 // Flat LayerNorm plan with 12-byte lane chunks (rwn_kernels.hpp) for rows of 12 * 2^k bytes,
 // 2^k <= 64 lanes, on 4-byte aligned operands.  Such rows in 16-byte chunks leave a quarter of
-// their lanes idle, or are not whole chunks at all.  Measured at LayerNorm 401408 x 24 float32
-// on one MI355X against the 16-byte flat kernels: forward 16.3 -> 15.4 us, backward stage 1
-// 21.1 -> 20.5 us.  Four waves per workgroup (fewer for small M); tiles are the waves' row
-// groups (the forward's two steps of them), dealt round-robin over a persistent grid.
+// their lanes idle, or are not whole chunks at all.  Measured on one MI355X against the 16-byte
+// flat kernels (traced us, forward / backward stage 1): LayerNorm 401408 x 24 float32 16.4 / 22.1
+// -> 15.3 / 21.9; 262144 x 48 float32 21.1 / 27.6 -> 19.0 / 27.2; 65536 x 384 bf16 23.4 / 35.1 ->
+// 21.8 / 35.3.  Four waves per workgroup (fewer for small M); tiles are the waves' row groups
+// (the forward's two steps of them), dealt round-robin over a persistent grid.
 static bool plan_flat12(bool backward, int64_t M, int64_t N, int xdt, int pdt, int cus, bool occupancy,
                         int wg_per_cu, int min_waves, Plan* pp) {
     const int esz = xdt == DT_F32 ? 4 : 2;
