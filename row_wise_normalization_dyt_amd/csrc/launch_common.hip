@@ -25,8 +25,8 @@ static int64_t next_pow2(int64_t v) {
 
 // Tuning overrides, read once (each changes the launch plan, and with it the reduction order
 // and so the low bits of parameter gradients):
-//   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4; default:
-//                           chosen per shape)
+//   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4; default: 2
+//                           for DyT, 1 otherwise)
 //   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
 //   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
@@ -288,7 +288,7 @@ static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pd
 
 bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int misalign_bytes,
                int cus, bool occupancy, Plan* out, int layout) {
-    static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 1);
+    static const int fwd_rt = env_int("RWN_FWD_RT", 1, 4, 0);
     static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 0);
     static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
     static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
@@ -428,11 +428,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.tpr = 64 * best_w;
     }
     const bool narrow_aligned = p.mode == MODE_ALIGNED && p.cpt == 1 && p.tpr <= 64;
-    // Narrow DyT backwards of 32 lanes per row (N = 256 bf16) run fastest with two rows per
-    // thread and no pipelining (measured 311 -> 297 us at M = 1048573); other narrow shapes
-    // with one (two rows per thread measured 4.6% slower for LayerNorm N = 24 fp32).
-    const int bwd_rt_auto = (layer == LAYER_DYT && p.tpr >= 32) ? 2 : 1;
-    p.rt = narrow_aligned ? (backward ? (bwd_rt > 0 ? bwd_rt : bwd_rt_auto) : fwd_rt) : 1;
+    // Narrow DyT rows run fastest with two rows per thread (one tile ahead in forwards and in
+    // backwards of up to 16 lanes per row, no pipelining above: see the pipelining rule below);
+    // other narrow shapes with one (two rows per thread measured 4.6% slower for LayerNorm
+    // N = 24 fp32).
+    const int rt_auto = layer == LAYER_DYT ? 2 : 1;
+    p.rt = narrow_aligned ? (backward ? (bwd_rt > 0 ? bwd_rt : rt_auto) : (fwd_rt > 0 ? fwd_rt : rt_auto)) : 1;
     if (p.rt == 3) p.rt = 2;
     if (layout) p.rt = 1;
 
@@ -460,12 +461,21 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // the SHIFTED LayerNorm / RMSNorm ones) and in 16-wave rows, and in SHIFTED backwards;
     // elsewhere the doubled input registers cost more than the overlap gains.  Shapes with
     // more than two chunks per thread have no pipelined form.
-    // Narrow DyT rows (the most arithmetic per byte) gain from running two tiles ahead: in the
-    // backward always, in the forward from 16 lanes per row up.
+    // Narrow DyT rows (the most arithmetic per byte) take two rows per thread, one tile ahead
+    // (below); with one row per thread (RWN_FWD_RT / RWN_BWD_RT = 1) they run two tiles ahead in
+    // the backward always, in the forward from 16 lanes per row up.
     if (p.cpt * p.rt <= 2) {
         const bool one = p.cpt * p.rt == 1;
         const bool narrow_dyt = layer == LAYER_DYT && one && p.mode == MODE_ALIGNED && p.tpr <= 64;
+        // Narrow DyT with two rows per thread (1048573 x N bf16, traced us against one row per
+        // thread, one or two tiles ahead): forwards one tile ahead, N = 32 28.0 -> 25.8, 128
+        // 102.8 -> 99.5, 256 208.8 -> 196.3 (fp32 N = 256: 104.0 -> 93.7); backwards one tile
+        // ahead up to 16 lanes per row, N = 32 41.4 -> 40.4, 128 154.8 -> 145.3 (fp32 N = 64: 38.5
+        // -> 36.8), and not pipelined from 32 lanes (fp32 N = 256 one tile ahead 132.5 -> 141.1).
+        const bool narrow_dyt2 = layer == LAYER_DYT && p.cpt == 1 && p.rt == 2 && p.mode == MODE_ALIGNED &&
+                                 p.tpr <= 64;
         if (prefetch >= 0) p.pf = (prefetch == 2 && !(one && p.mode != MODE_SCALAR)) ? 1 : prefetch;
+        else if (narrow_dyt2) p.pf = (!backward || p.tpr <= 16) ? 1 : 0;
         else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
         else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
         else if (layer == LAYER_RMS && p.mode == MODE_ALIGNED && p.tpr >= 128 &&
