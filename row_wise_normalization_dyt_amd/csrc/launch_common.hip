@@ -148,21 +148,26 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     const int V = 16 / esz;
     const int64_t nm = N / V;   // most whole chunks a row can hold (a row starting aligned)
     // Chunks per lane, in order of preference; the fewest lane slots win and ties go to the
-    // earlier entry.  Measured at 65536 x {1025, 2049, 4097} bf16 and 65536 x 1025 float32
-    // (forward / backward us): LayerNorm and RMSNorm backwards run fastest with 8 elements per
-    // lane (bf16 N = 2049: 1 chunk 142.4 / 132.2 against 2 chunks 178.2 / 151.2; N = 4097: 286.2 /
-    // 275.5 against 356.9 / 302.6; float32 N = 1025: 2 chunks 149.7 / 147.2 against 4 chunks
-    // 154.6 / 153.3 and 1 chunk 212.3 / 156.7), their forwards with 2 chunks (bf16 N = 2049
-    // LayerNorm 105.5 against 118.9 with 1; float32 N = 1025 98.0 against 107.5 with 4), and DyT
-    // with 16 elements per lane (bf16 N = 2049 backward 178.5 against 183.4 with 1 chunk; float32
-    // N = 1025 forward 108.5 / backward 158.0 with 4 chunks against 113.5 / 174.4 with 2).  32
-    // elements per lane (4 bfloat16 chunks) only for LayerNorm / RMSNorm rows too wide for 8
+    // earlier entry.  Measured at 65536 x N (forward / backward traced us):
+    //   - LayerNorm and RMSNorm backwards run fastest with one chunk per lane: bf16 N = 2049
+    //     142.4 / 132.2 against 178.2 / 151.2 with two, N = 4097 286.2 / 275.5 against 356.9 /
+    //     302.6; float32 N = 1025 131.6 / 133.7 against 148.8 / 146.3 with two, N = 2049 267.8 /
+    //     265.1 against 299.1 / 293.0 (aligned N = 1024 no slower).
+    //   - Their forwards run fastest with two (bf16 N = 2049 LayerNorm 105.5 against 118.9 with
+    //     one, RMSNorm N = 2048 85.8 against 101.1; float32 N = 1025 LayerNorm 98.0 against 112.7),
+    //     except 16-bit RMSNorm rows off the 16-byte grid that two chunks fit in one wave: N = 1025
+    //     54.3 against 52.8 with one chunk on two waves (float16 54.1 against 52.3); aligned N = 1024
+    //     measured 47.0 against 50.0, so it keeps two.
+    //   - DyT runs fastest with 16 elements per lane (bf16 N = 2049 backward 178.5 against 183.4
+    //     with one chunk; float32 N = 1025 forward 108.5 / backward 158.0 with four chunks against
+    //     113.5 / 174.4 with two).
+    // 32 elements per lane (4 bfloat16 chunks) only for LayerNorm / RMSNorm rows too wide for 8
     // waves otherwise: DyT's backward would spill there.
     int cands[3];
     if (layer == LAYER_DYT) {
         if (V == 8) { cands[0] = 2; cands[1] = 1; cands[2] = 4; }
         else { cands[0] = 4; cands[1] = 2; cands[2] = 1; }
-    } else if (backward && V == 8) {
+    } else if (backward || (layer == LAYER_RMS && V == 8 && nm <= 128 && (N % V != 0 || b != 0))) {
         cands[0] = 1; cands[1] = 2; cands[2] = 4;
     } else if (V == 8) {
         cands[0] = 2; cands[1] = 1; cands[2] = 4;
