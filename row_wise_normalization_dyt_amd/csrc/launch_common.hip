@@ -26,7 +26,7 @@ static int64_t next_pow2(int64_t v) {
 // Tuning overrides, read once (each changes the launch plan, and with it the reduction order
 // and so the low bits of parameter gradients):
 //   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4; default: 2
-//                           for DyT, 1 otherwise)
+//                           for DyT and 16-bit RMSNorm, 1 otherwise)
 //   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
 //   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
@@ -434,10 +434,14 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     }
     const bool narrow_aligned = p.mode == MODE_ALIGNED && p.cpt == 1 && p.tpr <= 64;
     // Narrow DyT rows run fastest with two rows per thread (one tile ahead in forwards and in
-    // backwards of up to 16 lanes per row, no pipelining above: see the pipelining rule below);
-    // other narrow shapes with one (two rows per thread measured 4.6% slower for LayerNorm
-    // N = 24 fp32).
-    const int rt_auto = layer == LAYER_DYT ? 2 : 1;
+    // backwards of up to 16 lanes per row, no pipelining above: see the pipelining rule below).
+    // So do narrow 16-bit RMSNorm rows, not pipelined (traced fwd / bwd us, one -> two rows per
+    // thread): 1048576 x 32 bf16 26.5 / 42.2 -> 25.8 / 37.9, x 64 50.4 / 75.0 -> 47.4 / 70.7,
+    // x 128 100.2 / 145.3 -> 93.8 / 140.0, f16 x 128 97.6 / 147.1 -> 94.0 / 140.9, 524288 x 256
+    // bf16 99.0 / 146.5 -> 94.7 / 141.1.  fp32 RMSNorm keeps one (1048576 x 128 backward 275.6 ->
+    // 295.2), and so do narrow LayerNorm rows, which take the flat kernels (two rows per thread
+    // on the general kernels: 1048576 x 128 bf16 forward 97.5 -> 103.0, N = 24 fp32 4.6% slower).
+    const int rt_auto = (layer == LAYER_DYT || (layer == LAYER_RMS && esz == 2)) ? 2 : 1;
     p.rt = narrow_aligned ? (backward ? (bwd_rt > 0 ? bwd_rt : rt_auto) : (fwd_rt > 0 ? fwd_rt : rt_auto)) : 1;
     if (p.rt == 3) p.rt = 2;
     if (layout) p.rt = 1;
