@@ -238,6 +238,22 @@ def test_dyt_alpha_edges_full_rows(alpha, N):
     tol.assert_reports(reps)
 
 
+@pytest.mark.parametrize("alpha", [-0.5, -3.0, -0.0, -math.inf, 2.0 ** -40, -(2.0 ** 40), 1e-20, 1e20, 3e38])
+def test_dyt_alpha_values(alpha):
+    """Alphas on both sides of the DyT kernels' per-launch constants and backward fast path:
+    negative (its sign applied to gamma and to the dgamma sums), -0, -inf, the fast path's
+    bounds 2^-40 and 2^40, and magnitudes past them (formed element by element from alpha x).
+    Narrow (general kernels, SCALAR mode) and wide (split) shapes, every output against the
+    oracle."""
+    reps = []
+    for (M, N, xdt, pdt) in ((4099, 24, "f32", "f32"), (1031, 32, "bf16", "f32"), (515, 17, "f16", "f32"),
+                             (257, 1025, "bf16", "bf16"), (67, 4096, "f32", "f32")):
+        wl = workloads.small("dyt", M, N, xdt, pdt, seed=M + N, alpha=alpha)
+        _banner(wl, "alpha", alpha)
+        reps += gc.check_workload(wl, DEV)
+    tol.assert_reports(reps)
+
+
 # ----------------------------------------------------------------- full-size workloads
 
 FULL = [n for n in workloads.WORKLOADS]
@@ -362,11 +378,17 @@ def test_full_size_workload(name):
                                                ("layernorm", 40000, 1025, "bf16", "f32")])
 def test_multi_tile_workgroups_all_rows(layer, M, N, xdt, pdt):
     """Shapes where every workgroup of the persistent grids walks several tiles, so the
-    pipelined tile loops rotate through all of their buffers; every element compared."""
+    pipelined tile loops rotate through all of their buffers; every element compared.  The
+    grids follow the kernels' residency on the device, so M grows (up to 4x) until one of the
+    two grids has at least four tiles per workgroup."""
+    for _ in range(3):
+        pf = rwn.plan(layer, False, M, N, gc.DT[xdt], param_dtype=gc.DT[pdt])
+        pb = rwn.plan(layer, True, M, N, gc.DT[xdt])
+        if pf["ntiles"] >= 4 * pf["grid"] // pf["ncb"] or pb["ntiles"] >= 4 * pb["grid"] // pb["ncb"]:
+            break
+        M = 2 * M + 37
+    assert pf["ntiles"] >= 4 * pf["grid"] // pf["ncb"] or pb["ntiles"] >= 4 * pb["grid"] // pb["ncb"], (M, pf, pb)
     wl = workloads.small(layer, M, N, xdt, pdt, seed=M + N)
-    pf = rwn.plan(layer, False, M, N, gc.DT[xdt], param_dtype=gc.DT[pdt])
-    pb = rwn.plan(layer, True, M, N, gc.DT[xdt])
-    assert pf["ntiles"] >= 4 * pf["grid"] // pf["ncb"] or pb["ntiles"] >= 4 * pb["grid"] // pb["ncb"]
     _banner(wl, "multi-tile", pf["ntiles"] * pf["ncb"] / pf["grid"], pb["ntiles"] * pb["ncb"] / pb["grid"])
     reps = gc.check_full_rows(wl, DEV)
     tol.assert_reports(reps)
