@@ -36,6 +36,8 @@ static int64_t next_pow2(int64_t v) {
 //                           (default: XCD-contiguous for rows of a wave or more only)
 //   RWN_WIDE_CPT            1, 2 or 4: chunks per thread of wide LayerNorm / RMSNorm rows
 //   RWN_PACKED_ROWS         0: SHIFTED DyT rows take whole waves (default 1: packed rows)
+//   RWN_NARROW_SHIFTED      0: narrow rows not aligned to 16-byte chunks move one element per
+//                           lane (SCALAR) instead of 16-byte chunks (default 1)
 //   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
 //                           they exist (and with it the general LayerNorm kernels)
 //   RWN_FLAT                0: narrow aligned LayerNorm rows take the general kernels (default 1:
@@ -306,6 +308,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int flat_rows = env_int("RWN_FLAT", 0, 1, 1);
     static const int split_rows = env_int("RWN_SPLIT", 0, 2, 1);
     static const int flat12_rows = env_int("RWN_FLAT12", 0, 1, 1);
+    static const int narrow_shifted = env_int("RWN_NARROW_SHIFTED", 0, 1, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -322,8 +325,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         chunks = N / V;
     } else {
         // A row that starts V-1 elements past a 16-byte boundary spans this many chunks.
+        // Narrow rows take the same 16-byte chunks (a power-of-two group of lanes per row, several
+        // rows per workgroup, each row slot with the shift of its rows; strided rows all share the
+        // base's) rather than one element per lane: at 64 MiB tensors, bf16 N = 100 ran at 20-22%
+        // of 8 TB/s per step in SCALAR mode for all three layers.
         const int64_t cs = (N + V - 1 + V - 1) / V;
-        if (cs > 64) {
+        if (cs > 64 || (narrow_shifted && layout <= 1)) {
             p.mode = MODE_SHIFTED;
             p.base_shift = b;
             chunks = cs;
@@ -350,7 +357,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // 268.2 -> 273.0 us.
     const bool few_rows = M <= (int64_t)64 * cus;
     int split_max_w = 0;
-    if (p.mode == MODE_SHIFTED) split_max_w = 8;
+    if (p.mode == MODE_SHIFTED && chunks > 64) split_max_w = 8;
     else if (p.mode == MODE_ALIGNED && chunks > 64)
         split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
     if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
@@ -447,14 +454,19 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     if (layout) p.rt = 1;
 
     // Row slots: narrow rows fill 256-thread workgroups; wide rows use wide_block threads.
-    // SHIFTED slots each carry their own shift, so a strided SHIFTED workgroup has one slot,
-    // except packed DyT rows, whose slots keep their shifts because the tile stride is a
-    // multiple of V.
+    // SHIFTED slots each carry their own shift, so a strided SHIFTED workgroup of wide rows has
+    // one slot.  Narrow SHIFTED rows and packed DyT rows have several: their slots keep their
+    // shifts because the tile stride (grid * rpp rows, the grid a multiple of 8) is a multiple
+    // of V.
     // A blocked SHIFTED workgroup walks consecutive tiles, so its slots must be V rows apart
     // (rpp = V) for each slot to keep one shift; where V slots do not fit in a workgroup the
     // backward stays strided.
     bool blocked = backward && blocked_k > 0 && p.ncb == 1 && layout == 0;
-    if (p.mode == MODE_SHIFTED) {
+    if (p.mode == MODE_SHIFTED && p.tpr <= 64) {
+        // narrow rows: 256 threads, or V slots where that is more (whole waves, and slots V apart
+        // for a blocked backward)
+        p.rpp = std::max(256 / p.tpr, V);
+    } else if (p.mode == MODE_SHIFTED) {
         if (blocked && (int64_t)p.tpr * V <= max_block(p.rt, p.cpt, esz)) {
             p.rpp = V;
         } else {
@@ -483,10 +495,16 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         // -> 36.8), and not pipelined from 32 lanes (fp32 N = 256 one tile ahead 132.5 -> 141.1).
         const bool narrow_dyt2 = layer == LAYER_DYT && p.cpt == 1 && p.rt == 2 && p.mode == MODE_ALIGNED &&
                                  p.tpr <= 64;
+        // Narrow SHIFTED rows (measured at 64 MiB bf16 tensors, traced us): LayerNorm / RMSNorm
+        // forwards run one tile ahead (N = 100: 48.5 -> 46.0, 43.8 -> 41.6; N = 500: 39.4 -> 37.5,
+        // 33.9 -> 32.6; float32 LayerNorm N = 250: 103.6 -> 98.3), and DyT backwards do not
+        // (N = 500: 52.2 -> 47.7, N = 100: 56.7 -> 55.4).
+        const bool narrow_shift = p.mode == MODE_SHIFTED && p.tpr <= 64;
         if (prefetch >= 0) p.pf = (prefetch == 2 && !(one && p.mode != MODE_SCALAR)) ? 1 : prefetch;
         else if (narrow_dyt2) p.pf = (!backward || p.tpr <= 16) ? 1 : 0;
         else if (narrow_dyt && (backward || p.tpr >= 16)) p.pf = 2;
-        else if (!backward) p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED)) || p.tpr >= 1024) ? 1 : 0;
+        else if (!backward)
+            p.pf = ((one && (layer == LAYER_DYT || p.mode != MODE_SHIFTED || narrow_shift)) || p.tpr >= 1024) ? 1 : 0;
         else if (layer == LAYER_RMS && p.mode == MODE_ALIGNED && p.tpr >= 128 &&
                  (p.tpr >= 1024 || M <= (int64_t)32 * cus * std::max(1, wide_block / p.tpr)))
             // Aligned RMSNorm backwards of two or more waves per row, pipelined (measured): 16-wave
@@ -494,7 +512,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             // CU (16384 x 2048 and 8192 x 4096 bf16, 3-6% faster); with more tiles per CU, as at
             // 65536 x 4096..8192, it measured 3-7% slower.
             p.pf = 1;
-        else p.pf = (p.mode == MODE_SHIFTED && one && !packed) ? 1 : 0;
+        else p.pf = (p.mode == MODE_SHIFTED && one && !packed && !(layer == LAYER_DYT && narrow_shift)) ? 1 : 0;
     }
     // Narrow aligned LayerNorm rows, one chunk and one row per thread, take the flat kernels
     // (plain loads on clamped row indices, no per-tile descriptors), which run fastest without
@@ -518,7 +536,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     p.ntiles = (M + rows_per_tile - 1) / rows_per_tile;
     if (backward && (p.rpp > 1 || p.flat)) {   // LDS for combining the row slots' partials
         int64_t e = (int64_t)p.cpt * v_elems * p.block;
-        if (p.mode == MODE_SHIFTED && N > e) e = N;
+        if (p.mode == MODE_SHIFTED && (int64_t)p.rpp * N > e) e = (int64_t)p.rpp * N;   // a row per slot
         if (p.flat) e *= 2;   // the flat backward combines dgamma and dbeta together
         p.lds_bytes = (size_t)e * sizeof(float);
     }

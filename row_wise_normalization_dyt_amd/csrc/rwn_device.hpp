@@ -11,11 +11,11 @@
 //
 // Three modes handle every N and base address:
 //   ALIGNED  N % V == 0 and 16-byte-aligned rows: chunk c covers columns [cV, cV+V).
-//   SHIFTED  any N (wide rows only): row r starts s = (b + rN) mod V elements past a 16-byte
-//            boundary; chunk c covers columns [cV - s, cV - s + V).  The launcher makes every
-//            thread visit rows that share one s (grid * rpp divisible by V), so the column map
-//            is still fixed.  Chunks cut by the row ends are loaded/stored element by element.
-//   SCALAR   V = 1 (narrow rows whose chunks would not be 16-byte aligned).
+//   SHIFTED  any N: row r starts s = (b + rN) mod V elements past a 16-byte boundary; chunk c
+//            covers columns [cV - s, cV - s + V).  The launcher makes every thread visit rows
+//            that share one s (grid * rpp divisible by V), so the column map is still fixed.
+//            Chunks cut by the row ends are loaded/stored element by element.
+//   SCALAR   V = 1 (strided rows of mixed alignment).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -171,23 +171,25 @@ __device__ __forceinline__ void write_partial(float* __restrict__ out, int64_t c
     }
     const int nb = blockDim.x;
     if (MODE == MODE_SHIFTED) {
-        // Slots hold different column maps: add them into a column-indexed LDS row, one slot
-        // at a time (within a slot every column has one owner).  (Only single-column-block
-        // plans have SHIFTED slots, so the row is all of [0, N).)
-        __syncthreads();
-        for (int64_t j = threadIdx.x; j < g.N; j += nb) part[j] = 0.f;
-        for (int sl = 0; sl < g.rpp; ++sl) {
-            __syncthreads();
-            if (slot == sl) {
+        // Slots hold different column maps: each slot writes its sums into a column-indexed
+        // LDS row of its own (within a slot every column of [0, N) has exactly one owner), then
+        // each column adds the slots' rows in slot order.  `part` holds rpp * N floats here.
+        // (Only single-column-block plans have SHIFTED slots, so a row is all of [0, N).)
+        __syncthreads();   // previous users of `part` are done
+        if (slot < g.rpp) {
+            float* mine = part + (int64_t)slot * g.N;
 #pragma unroll
-                for (int k = 0; k < CPT; ++k)
+            for (int k = 0; k < CPT; ++k)
 #pragma unroll
-                    for (int v = 0; v < V; ++v)
-                        if (cm.valid(k, v, g.N)) part[cm.col0[k] + v] += acc[k * V + v];
-            }
+                for (int v = 0; v < V; ++v)
+                    if (cm.valid(k, v, g.N)) mine[cm.col0[k] + v] = acc[k * V + v];
         }
         __syncthreads();
-        for (int64_t j = threadIdx.x; j < g.N; j += nb) out[j * cs] = part[j];
+        for (int64_t j = threadIdx.x; j < g.N; j += nb) {
+            float sum = part[j];
+            for (int sl = 1; sl < g.rpp; ++sl) sum += part[(int64_t)sl * g.N + j];
+            out[j * cs] = sum;
+        }
         return;
     }
     if (g.tpr < 64) {

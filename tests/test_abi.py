@@ -173,7 +173,11 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
             if p["mode"] == 0:
                 assert N % V == 0 and mis == 0
             if p["mode"] == 1:
-                assert p["rt"] == 1 and (p["rpp"] == 1 or p["rpp"] % V == 0 or packed)
+                # one slot, or slots that keep their shifts: V apart (blocked), or revisited at a
+                # tile stride that is a multiple of V (checked below); narrow rows fill 256 threads
+                assert p["rt"] == 1 and (p["rpp"] == 1 or p["rpp"] % V == 0 or packed or p["tpr"] <= 64), p
+                if p["tpr"] <= 64 and not p["split"]:
+                    assert p["rpp"] * p["tpr"] == p["block"] == max(256, V * p["tpr"]), p
             rows_per_tile = p["rpp"] * p["rt"]
             assert p["ntiles"] * rows_per_tile >= M > (p["ntiles"] - 1) * rows_per_tile
             if p["strided"]:

@@ -138,6 +138,31 @@ def test_misaligned_operands_take_the_shifted_path(layer, offset, xdt):
 
 
 @pytest.mark.parametrize("layer", LAYERS)
+def test_narrow_rows_in_shifted_chunks(layer):
+    """Narrow rows that are not whole 16-byte chunks move in 16-byte chunks: a power-of-two lane
+    group per row, several row slots per workgroup (up to 128 at N = 3), each slot keeping its
+    rows' shift while its workgroup walks its tiles.  Row counts give every workgroup of the
+    backward's persistent grid at least two tiles; whole tensors compared, parameter gradients
+    combined over all slots."""
+    reps = []
+    for (N, xdt, pdt) in ((100, "bf16", "f32"), (500, "bf16", "bf16"), (17, "f16", "f16"), (3, "bf16", "f32"),
+                          (250, "f32", "f32"), (7, "f32", "f32")):
+        pb = rwn.plan(layer, True, 1 << 22, N, gc.DT[xdt])
+        assert pb["mode"] == 1 and pb["tpr"] <= 64 and not pb["split"], pb
+        M = 2 * pb["grid"] * pb["rpp"] + 37
+        for _ in range(4):   # the grid follows M (and the kernels' residency): grow M until it holds
+            pb = rwn.plan(layer, True, M, N, gc.DT[xdt])
+            if pb["ntiles"] >= 2 * pb["grid"]:
+                break
+            M = 2 * M + 37
+        assert pb["ntiles"] >= 2 * pb["grid"], (M, pb)
+        wl = workloads.small(layer, M, N, xdt, pdt, seed=M + N)
+        _banner(wl, "narrow shifted, tiles per workgroup", pb["ntiles"] / pb["grid"], "slots", pb["rpp"])
+        reps += gc.check_workload(wl, DEV)
+    tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("layer", LAYERS)
 def test_float16_outputs_overflow_to_infinity(layer):
     """float16 tops out at 65504: outputs whose exact value rounds beyond it are +-inf, and
     every other element stays within the usual bound (the oracle's exact values rounded to
@@ -243,7 +268,7 @@ def test_dyt_alpha_values(alpha):
     """Alphas on both sides of the DyT kernels' per-launch constants and backward fast path:
     negative (its sign applied to gamma and to the dgamma sums), -0, -inf, the fast path's
     bounds 2^-40 and 2^40, and magnitudes past them (formed element by element from alpha x).
-    Narrow (general kernels, SCALAR mode) and wide (split) shapes, every output against the
+    Narrow (general kernels, ALIGNED and SHIFTED chunks) and wide (split) shapes, every output against the
     oracle."""
     reps = []
     for (M, N, xdt, pdt) in ((4099, 24, "f32", "f32"), (1031, 32, "bf16", "f32"), (515, 17, "f16", "f32"),
