@@ -28,7 +28,9 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_FWD_RT, RWN_BWD_RT  rows per thread of narrow aligned plans (1, 2 or 4; default: 2
 //                           for DyT and 16-bit RMSNorm, 1 otherwise)
 //   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
-//   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16)
+//   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16; 8 for
+//                           backwards of 2-7-wave rows on the general kernels when rows are
+//                           few per CU)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
@@ -299,6 +301,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int bwd_rt = env_int("RWN_BWD_RT", 1, 4, 0);
     static const int wg_per_cu = env_int("RWN_WG_PER_CU", 1, 32, 0);
     static const int min_waves = env_int("RWN_MIN_WAVES", 1, 32, 16);
+    static const bool min_waves_set = getenv("RWN_MIN_WAVES") != nullptr;
     static const int wide_block = env_int("RWN_WIDE_BLOCK", 64, 1024, 512);
     static const int blocked_k = env_int("RWN_BLOCKED_K", 1, 1 << 20, 0);
     static const int xcd_remap = env_int("RWN_XCD_REMAP", 0, 1, -1);
@@ -559,7 +562,16 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.grid = (p.ntiles + p.kt - 1) / p.kt;
     } else {
         p.strided = 1;
-        persistent_grid(p, cus, occ, wg_per_cu, min_waves);
+        // Backwards of wide rows on the general kernels, two to seven waves per workgroup, with
+        // few rows per CU take half the resident waves (at least two workgroups per CU): with 16
+        // per CU the grid leaves each workgroup a handful of rows and a whole partial row to
+        // write for them (and stage 2 to read).  Measured at 64 MiB tensors (backward stage 1 +
+        // stage 2, us, 16 -> 8 waves): LayerNorm bf16 6553 x 5120 95.0 -> 66.6, float32 5592 x
+        // 3000 63.3 -> 46.3 and 3276 x 5120 59.1 -> 48.7, RMSNorm bf16 6553 x 5120 60.9 -> 49.0,
+        // DyT bf16 6553 x 5120 67.5 -> 53.0.  Forwards were mostly slower with it, and backwards
+        // of 8-wave workgroups mixed (float32 LayerNorm 4096 x 4096 45.8 -> 54.5).
+        const int mw = backward && few_rows && p.tpr >= 128 && p.tpr <= 448 && !min_waves_set ? 8 : min_waves;
+        persistent_grid(p, cus, occ, wg_per_cu, mw);
         p.kt = 0;
         // XCD-contiguous numbering pays where a row spans a wave or more (LayerNorm / RMSNorm
         // 65536 x 4096..8192 bf16: 4-6% faster): neighbouring rows share cache lines at their
