@@ -357,12 +357,19 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // 288.2 -> 332.0, 271.5 -> 284.3 us), and forwards of eight no faster (N = 8192).
     // RMSNorm backwards of 4-wave rows split as well when the rows are few per CU (at most 64):
     // 8192 x 4096 bf16 stage 1 43.2 -> 41.1 us, while at 65536 x 4096 the split form measured
-    // 268.2 -> 273.0 us.
+    // 268.2 -> 273.0 us.  16-bit LayerNorm rows of 512 chunks or more split up to 8 waves when
+    // they are few per CU (64 MiB tensors, forward / backward stage 1 us): bf16 4096 x 8192 38.6
+    // / 65.1 -> 27.1 / 45.0, 6553 x 5120 41.5 / 57.9 -> 34.2 / 45.9, 8192 x 4096 backward 54.8 ->
+    // 47.1; 12000 x 8192 step 54.7 -> 67.3% of 8 TB/s.  Narrower few rows measured slower split
+    // (bf16 11184 x 3000 backward 52.5 -> 67.1), and float32 rows no faster (3276 x 5120 step
+    // 46.1 -> 44.8%).
     const bool few_rows = M <= (int64_t)64 * cus;
     int split_max_w = 0;
     if (p.mode == MODE_SHIFTED && chunks > 64) split_max_w = 8;
     else if (p.mode == MODE_ALIGNED && chunks > 64)
-        split_max_w = split_rows == 2 ? 8 : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
+        split_max_w = split_rows == 2 || (layer == LAYER_LN && esz == 2 && few_rows && chunks >= 512)
+                          ? 8
+                          : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
     if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
         plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, xcd_remap,
                    split_max_w, &p)) {
