@@ -362,12 +362,16 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     // / 65.1 -> 27.1 / 45.0, 6553 x 5120 41.5 / 57.9 -> 34.2 / 45.9, 8192 x 4096 backward 54.8 ->
     // 47.1; 12000 x 8192 step 54.7 -> 67.3% of 8 TB/s.  Narrower few rows measured slower split
     // (bf16 11184 x 3000 backward 52.5 -> 67.1), and float32 rows no faster (3276 x 5120 step
-    // 46.1 -> 44.8%).
+    // 46.1 -> 44.8%).  RMSNorm and DyT do the same from 1024 chunks (bf16 N = 8192, step %:
+    // RMSNorm 4096 rows 48.8 -> 54.5, 12000 rows 64.2 -> 66.5; DyT 45.2 -> 48.7, 56.9 -> 62.8;
+    // at N = 3000 and 5120 they measured slower split).  Rows of 2048 chunks keep the general
+    // kernels (bf16 8000 x 16384 step %: RMSNorm 66.7 -> 62.2, LayerNorm 57.0 -> 54.7 split).
     const bool few_rows = M <= (int64_t)64 * cus;
     int split_max_w = 0;
     if (p.mode == MODE_SHIFTED && chunks > 64) split_max_w = 8;
     else if (p.mode == MODE_ALIGNED && chunks > 64)
-        split_max_w = split_rows == 2 || (layer == LAYER_LN && esz == 2 && few_rows && chunks >= 512)
+        split_max_w = split_rows == 2 || (esz == 2 && few_rows && chunks >= (layer == LAYER_LN ? 512 : 1024) &&
+                                          chunks <= 1024)
                           ? 8
                           : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
     if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
