@@ -144,7 +144,8 @@ static void partial_layout(int layer, Plan& p) {
 // per workgroup.  Returns false where no shape fits (float32 rows wider than 8192), leaving the
 // general kernels' shifted mode.
 static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int b, int cus,
-                       bool occupancy, int wg_per_cu, int min_waves, int xcd_remap, int max_w, Plan* pp) {
+                       bool occupancy, int wg_per_cu, int min_waves, bool auto_waves, int xcd_remap, int max_w,
+                       Plan* pp) {
     static const int split_cpt = env_int("RWN_SPLIT_CPT", 1, 4, 0);
     static const int split_pf = env_int("RWN_SPLIT_PF", 0, 1, -1);
     Plan& p = *pp;
@@ -234,7 +235,14 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     }
     p.strided = 1;
     p.kt = 0;
-    persistent_grid(p, cus, occ, wg_per_cu, min_waves);
+    // Workgroups of five to seven waves with two or more chunks per lane (3-wave row slots two
+    // to a workgroup, 5-7-wave slots alone) take two per CU rather than the 18-21 waves that 16
+    // rounds up to: bf16 44739 x 3000 forwards (256 MiB tensors) LayerNorm 122.3 -> 102.4 us,
+    // RMSNorm 108.2 -> 92.3, DyT 122.4 -> 117.0; 65536 x 2600 LayerNorm 161.2 -> 136.0.  With
+    // one chunk per lane that leaves too few bytes in flight (RMSNorm 65536 x 2300, 5-wave
+    // slots: forward 111.2 -> 173.1 us).
+    const int wpw = (p.block + 63) / 64;
+    persistent_grid(p, cus, occ, wg_per_cu, auto_waves && p.cpt >= 2 && wpw >= 5 && wpw <= 7 ? 8 : min_waves);
     const bool remap = xcd_remap >= 0 ? xcd_remap == 1 : true;
     p.xcd_remap = (remap && p.grid % 8 == 0) ? 1 : 0;
     if (backward) partial_layout(layer, p);
@@ -375,7 +383,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
                           ? 8
                           : (!backward || layer == LAYER_DYT || (layer == LAYER_RMS && few_rows)) ? 4 : 2;
     if (split_max_w && split_rows && prefetch < 0 && layout == 0 &&
-        plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, xcd_remap,
+        plan_split(layer, backward, M, N, xdt, pdt, b, cus, occupancy, wg_per_cu, min_waves, !min_waves_set, xcd_remap,
                    split_max_w, &p)) {
         *out = p;
         return true;
