@@ -240,9 +240,14 @@ static bool plan_split(int layer, bool backward, int64_t M, int64_t N, int xdt, 
     // rounds up to: bf16 44739 x 3000 forwards (256 MiB tensors) LayerNorm 122.3 -> 102.4 us,
     // RMSNorm 108.2 -> 92.3, DyT 122.4 -> 117.0; 65536 x 2600 LayerNorm 161.2 -> 136.0.  With
     // one chunk per lane that leaves too few bytes in flight (RMSNorm 65536 x 2300, 5-wave
-    // slots: forward 111.2 -> 173.1 us).
+    // slots: forward 111.2 -> 173.1 us); such LayerNorm backwards take at least 12 waves
+    // instead (two or three workgroups per CU: bf16 65536 x 1500 161.2 -> 119.2 us, 65536 x 2300
+    // 237.7 -> 183.9), while RMSNorm's ran slower that way (65536 x 1500 106.5 -> 115.4) and
+    // DyT's unchanged; forwards keep 16.
     const int wpw = (p.block + 63) / 64;
-    persistent_grid(p, cus, occ, wg_per_cu, auto_waves && p.cpt >= 2 && wpw >= 5 && wpw <= 7 ? 8 : min_waves);
+    int mw = min_waves;
+    if (auto_waves && wpw >= 5 && wpw <= 7) mw = p.cpt >= 2 ? 8 : (backward && layer == LAYER_LN) ? 12 : min_waves;
+    persistent_grid(p, cus, occ, wg_per_cu, mw);
     const bool remap = xcd_remap >= 0 ? xcd_remap == 1 : true;
     p.xcd_remap = (remap && p.grid % 8 == 0) ? 1 : 0;
     if (backward) partial_layout(layer, p);
