@@ -315,6 +315,31 @@ def test_flat_plans(backward):
     assert p["flat"] == 2 and p["xcd_remap"] == 0 and p["tpr"] == 8
 
 
+def test_planner_rules_off_grid_rows_and_few_rows():
+    """Plan choices that measured rules fix (cus = 256, no occupancy query).  Narrow rows off
+    the 16-byte grid move in 16-byte SHIFTED chunks: a power-of-two lane group per row and
+    max(256 / tpr, V) row slots, with no pipelining in DyT backwards.  With few rows per CU
+    (64 MiB bf16 tensors), 16-bit LayerNorm rows of 512-1024 chunks and RMSNorm / DyT rows of
+    1024 chunks take the split-row kernels in both directions; rows of 2048 chunks, narrower
+    RMSNorm rows and the same widths with many rows (65536) keep the general backward."""
+    bf, f32 = torch.bfloat16, torch.float32
+    p = rwn.plan("layernorm", False, 335544, 100, bf, param_dtype=f32, cus=256)
+    assert (p["mode"], p["tpr"], p["rpp"], p["split"]) == (1, 16, 16, 0), p
+    p = rwn.plan("rmsnorm", True, 1 << 20, 3, bf, cus=256)
+    assert (p["mode"], p["tpr"], p["rpp"], p["split"]) == (1, 2, 128, 0), p
+    p = rwn.plan("dyt", True, 67108, 500, bf, cus=256)
+    assert (p["mode"], p["tpr"], p["rpp"], p["prefetch"]) == (1, 64, 8, 0), p
+    for layer, N, few_split in (("layernorm", 4096, 1), ("layernorm", 8192, 1), ("layernorm", 3000, 0),
+                                ("layernorm", 16384, 0), ("rmsnorm", 8192, 1), ("rmsnorm", 5120, 0),
+                                ("dyt", 8192, 1), ("dyt", 16384, 0)):
+        M = (64 << 20) // (2 * N)
+        pb = rwn.plan(layer, True, M, N, bf, cus=256)
+        assert pb["split"] == few_split, (layer, N, pb)
+        if few_split:
+            assert rwn.plan(layer, False, M, N, bf, param_dtype=f32, cus=256)["split"] == 1, (layer, N)
+        assert rwn.plan(layer, True, 65536, N, bf, cus=256)["split"] == 0, (layer, N)
+
+
 def test_plan_is_deterministic():
     a = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
     b = [rwn.plan(l, b, 65536, 1025, torch.bfloat16, 2, cus=256) for l in ("dyt", "rmsnorm") for b in (0, 1)]
