@@ -29,8 +29,8 @@ static int64_t next_pow2(int64_t v) {
 //                           for DyT and 16-bit RMSNorm, 1 otherwise)
 //   RWN_WG_PER_CU           workgroups per CU of persistent grids (default: chosen per shape)
 //   RWN_MIN_WAVES           minimum resident waves per CU the grid must provide (16; 8 for
-//                           backwards of 5-7-wave rows on the general kernels, and of 2-4-wave
-//                           rows when rows are few per CU)
+//                           backwards of 5-7-wave rows on the general kernels, and of 2-4- and
+//                           9-15-wave rows when rows are few per CU)
 //   RWN_WIDE_BLOCK          workgroup size for wide rows (64..1024)
 //   RWN_BLOCKED_K           > 0: backward workgroups take this many consecutive tiles instead
 //                           of striding (fwd stays strided)
@@ -586,11 +586,12 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         p.grid = (p.ntiles + p.kt - 1) / p.kt;
     } else {
         p.strided = 1;
-        // Backwards of wide rows on the general kernels take half the resident waves (at least
-        // two workgroups per CU) with five to seven waves per workgroup, and with two to four
-        // when rows are few per CU: with 16 per CU the grid leaves each workgroup a handful of
-        // rows and a whole partial row to write for them (and stage 2 to read), and 5-7-wave
-        // workgroups run 18-21 waves per CU.  Measured (backward stage 1 + stage 2, us, 16 -> 8
+        // Backwards of wide rows on the general kernels take half the resident waves with rows of
+        // five to seven waves, and with rows of two to four or nine to fifteen when rows are few
+        // per CU: with 16 per CU the grid leaves each workgroup a handful of rows and a whole
+        // partial row to write for them (and stage 2 to read), and 5-7-wave workgroups run 18-21
+        // waves per CU.  (float32 3276 x 5120, 10-wave rows, backward stage 1 + stage 2 us:
+        // LayerNorm 59.1 -> 48.7, RMSNorm 45.8 -> 39.8, DyT 45.3 -> 42.1.)  Measured (backward stage 1 + stage 2, us, 16 -> 8
         // waves): 64 MiB tensors, LayerNorm bf16 6553 x 5120 95.0 -> 66.6, float32 5592 x 3000
         // 63.3 -> 46.3, RMSNorm bf16 6553 x 5120 60.9 -> 49.0, DyT bf16 6553 x 5120 67.5 -> 53.0;
         // 256 MiB tensors, LayerNorm bf16 26214 x 5120 235.1 -> 176.3, RMSNorm 210.2 -> 161.3,
@@ -598,9 +599,9 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
         // with many rows per CU run slower with it (LayerNorm bf16 65536 x 4096 289.7 -> 341.4),
         // forwards were mostly slower, and 8-wave backwards mixed (float32 LayerNorm 4096 x 4096
         // 45.8 -> 54.5).
-        const int mw = backward && p.tpr >= 128 && p.tpr <= 448 && (few_rows || p.tpr >= 320) && !min_waves_set
-                           ? 8
-                           : min_waves;
+        const int rw = p.tpr / 64;   // waves per row
+        const bool fewer = rw >= 5 && rw <= 7 ? true : few_rows && ((rw >= 2 && rw <= 4) || (rw >= 9 && rw <= 15));
+        const int mw = backward && fewer && !min_waves_set ? 8 : min_waves;
         persistent_grid(p, cus, occ, wg_per_cu, mw);
         p.kt = 0;
         // XCD-contiguous numbering pays where a row spans a wave or more (LayerNorm / RMSNorm
