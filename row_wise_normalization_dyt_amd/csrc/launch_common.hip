@@ -40,6 +40,8 @@ static int64_t next_pow2(int64_t v) {
 //   RWN_PACKED_ROWS         0: SHIFTED DyT rows take whole waves (default 1: packed rows)
 //   RWN_NARROW_SHIFTED      0: narrow rows not aligned to 16-byte chunks move one element per
 //                           lane (SCALAR) instead of 16-byte chunks (default 1)
+//   RWN_DYT_FLAT12          0: DyT rows of 12 * 2^k bytes take the general kernels instead of
+//                           the 12-byte ones (default 1)
 //   RWN_PREFETCH            0 / 1 / 2: force the plain / one-ahead / two-ahead tile loop where
 //                           they exist (and with it the general LayerNorm kernels)
 //   RWN_FLAT                0: narrow aligned LayerNorm rows take the general kernels (default 1:
@@ -263,7 +265,7 @@ static int resident_wgs(int layer, bool backward, const Plan& p, int xdt, int pd
 // -> 15.3 / 21.9; 262144 x 48 float32 21.1 / 27.6 -> 19.0 / 27.2; 65536 x 384 bf16 23.4 / 35.1 ->
 // 21.8 / 35.3.  Four waves per workgroup (fewer for small M); tiles are the waves' row groups
 // (the forward's two steps of them), dealt round-robin over a persistent grid.
-static bool plan_flat12(bool backward, int64_t M, int64_t N, int xdt, int pdt, int cus, bool occupancy,
+static bool plan_flat12(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt, int cus, bool occupancy,
                         int wg_per_cu, int min_waves, Plan* pp) {
     const int esz = xdt == DT_F32 ? 4 : 2;
     if ((N * esz) % 12) return false;
@@ -291,14 +293,14 @@ static bool plan_flat12(bool backward, int64_t M, int64_t N, int xdt, int pdt, i
         for (int i = 0; i < 3; ++i) {
             if (pdt >= 0 && pdts[i] != pdt) continue;
             if (!dtype_pair_ok(xdt, pdts[i])) continue;
-            const int n = resident_wgs(LAYER_LN, backward, p, xdt, pdts[i]);
+            const int n = resident_wgs(layer, backward, p, xdt, pdts[i]);
             if (n > 0) occ = occ == 0 ? n : std::min<int64_t>(occ, n);
         }
     }
     p.strided = 1;
     persistent_grid(p, cus, occ, wg_per_cu, min_waves);
     p.xcd_remap = 0;   // narrow rows stream faster in the hardware's workgroup order
-    if (backward) partial_layout(LAYER_LN, p);
+    if (backward) partial_layout(layer, p);
     return true;
 }
 
@@ -325,6 +327,7 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
     static const int split_rows = env_int("RWN_SPLIT", 0, 2, 1);
     static const int flat12_rows = env_int("RWN_FLAT12", 0, 1, 1);
     static const int narrow_shifted = env_int("RWN_NARROW_SHIFTED", 0, 1, 1);
+    static const int dyt_flat12 = env_int("RWN_DYT_FLAT12", 0, 1, 1);
     Plan p;
     p.M = M;
     p.N = N;
@@ -355,9 +358,16 @@ bool make_plan(int layer, bool backward, int64_t M, int64_t N, int xdt, int pdt,
             chunks = N;
         }
     }
-    if (flat_rows && flat12_rows && layer == LAYER_LN && layout == 0 && prefetch < 0 && blocked_k == 0 &&
-        misalign_bytes % 4 == 0 &&
-        plan_flat12(backward, M, N, xdt, pdt, cus, occupancy, wg_per_cu, min_waves, &p)) {
+    // DyT takes the 12-byte kernels for backwards, and for forwards of rows that are not whole
+    // 16-byte chunks: elsewhere the general forward (two rows per thread, one tile ahead)
+    // measured faster.  64 MiB tensors, traced us, general -> 12-byte: bf16 backwards N = 24
+    // 45.7 -> 40.8, 96 45.8 -> 41.4, 192 51.6 -> 42.6, 384 52.0 -> 47.4; float32 N = 12 37.6 ->
+    // 34.2; bf16 N = 12 (24-byte rows) forward 76.0 -> 32.0, backward 96.7 -> 40.9; forwards of
+    // whole chunks 25.0 -> 29.7 (float32 N = 12), 29.4 -> 32.0 (bf16 N = 24).
+    const bool dyt12 = layer == LAYER_DYT && dyt_flat12 && (backward || (N * esz) % 16 != 0 || misalign_bytes % 16);
+    if (flat_rows && flat12_rows && (layer == LAYER_LN || dyt12) && layout == 0 &&
+        prefetch < 0 && blocked_k == 0 && misalign_bytes % 4 == 0 &&
+        plan_flat12(layer, backward, M, N, xdt, pdt, cus, occupancy, wg_per_cu, min_waves, &p)) {
         *out = p;
         return true;
     }

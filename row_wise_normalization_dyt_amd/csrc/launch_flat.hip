@@ -1,6 +1,6 @@
 // Launchers of the flat LayerNorm kernels (narrow rows; p.flat 1: 16-byte chunks on aligned rows,
 // 2: 12-byte chunks): every dtype pair, group size 1..64 lanes, with and without
-// parameter-gradient partials and given statistics.
+// parameter-gradient partials and given statistics; and of the 12-byte DyT kernels.
 #include "rwn_kernels.hpp"
 #include "rwn_launch.hpp"
 
@@ -89,6 +89,59 @@ int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt) {
             else
                 k = backward ? (const void*)ln_bwd_flat_kernel<T, PT, R, 3, 1>
                              : (const void*)ln_fwd_flat_kernel<T, PT, R>;
+            n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
+            return hipSuccess;
+        });
+    });
+    return n;
+}
+
+// DyT in 12-byte chunks (p.flat == 2 only).
+hipError_t launch_dyt_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                               const void* gamma, const void* beta, void* y, hipStream_t s) {
+    if (p.flat != 2 || p.block > 256 || p.block < 1 || p.block % 64) return hipErrorInvalidConfiguration;
+    const Geom g = make_geom(p);
+    return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_tpr(p, [&](auto tpr) {
+            constexpr int R = decltype(tpr)::value;
+            if (p.rt != flat12_rt<R>()) return hipErrorInvalidValue;
+            return launch(dyt_fwd_flat12_kernel<T, PT, R, flat12_rt<R>()>, dim3((unsigned)p.grid),
+                          dim3(p.block), 0, s, (const T*)x, (const PT*)alpha, (const PT*)gamma,
+                          (const PT*)beta, (T*)y, g);
+        });
+    });
+}
+
+hipError_t launch_dyt_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                               const void* alpha, const void* gamma, void* dx, float* ws, hipStream_t s) {
+    if (p.flat != 2 || p.block > 256 || p.block < 1 || p.block % 64) return hipErrorInvalidConfiguration;
+    if (p.rt != 1) return hipErrorInvalidValue;
+    const Geom g = make_geom(p);
+    return dispatch_pg(ws, [&](auto pg) {
+        return dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+            using T = typename decltype(tt)::type;
+            using PT = typename decltype(pt)::type;
+            return dispatch_tpr(p, [&](auto tpr) {
+                constexpr int R = decltype(tpr)::value, G = decltype(pg)::value;
+                return launch(dyt_bwd_flat12_kernel<T, PT, R, G>, dim3((unsigned)p.grid), dim3(p.block),
+                              p.lds_bytes, s, (const T*)x, (const T*)dy, (const PT*)alpha, (const PT*)gamma,
+                              (T*)dx, ws, g);
+            });
+        });
+    });
+}
+
+int resident_wgs_dyt_flat(bool backward, const Plan& p, int xdt, int pdt) {
+    int n = 0;
+    (void)dispatch_dtypes(xdt, pdt, [&](auto tt, auto pt) {
+        using T = typename decltype(tt)::type;
+        using PT = typename decltype(pt)::type;
+        return dispatch_tpr(p, [&](auto tpr) {
+            constexpr int R = decltype(tpr)::value;
+            const void* k = backward ? (const void*)dyt_bwd_flat12_kernel<T, PT, R, 1>
+                                     : (const void*)dyt_fwd_flat12_kernel<T, PT, R, flat12_rt<R>()>;
             n = kernel_occupancy(k, p.block, backward ? p.lds_bytes : 0);
             return hipSuccess;
         });

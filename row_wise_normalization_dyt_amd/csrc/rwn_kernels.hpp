@@ -1007,6 +1007,117 @@ ln_bwd_flat12_kernel(const T* __restrict__ x, const T* __restrict__ dy, const fl
     }
 }
 
+// DyT in 12-byte lane chunks (rows of 12 * 2^k bytes: float32 N = 3 * 2^k, 16-bit N = 6 * 2^k),
+// the row and tile layout of the 12-byte LayerNorm kernels above.  The per-element arithmetic is
+// the general DyT kernels' (tanh_only, tanh_sech2, the same sums in the same order per lane).
+template <typename T, typename PT, int TPR, int RT>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256)))
+dyt_fwd_flat12_kernel(const T* __restrict__ x, const PT* __restrict__ alpha_p, const PT* __restrict__ gamma,
+                      const PT* __restrict__ beta, T* __restrict__ y, Geom g) {
+    constexpr int V = Words12<T>::V;
+    constexpr int R = 64 / TPR;      // rows per wave and step
+    const int wl = threadIdx.x & 63, grp = wl / TPR, lane = wl % TPR;
+    const int wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)lane * V;
+    float ga[V], be[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        ga[v] = to_f32(gamma[col + v]);
+        be[v] = to_f32(beta[col + v]);
+    }
+    const float alpha = to_f32(alpha_p[0]);
+    const int64_t rows_per_tile = g.rpp * RT;
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        const int64_t base = tile * rows_per_tile + (int64_t)wave * (RT * R);
+        Words12<T> xr[RT];
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            const int64_t row = base + j * R + grp;
+            xr[j].load(x + (row < g.M ? row : g.M - 1) * g.N + col, true);
+        }
+        // every step's outputs before the first store (see ln_fwd_flat12_kernel)
+        float o[RT][V];
+#pragma unroll
+        for (int j = 0; j < RT; ++j)
+#pragma unroll
+            for (int v = 0; v < V; ++v) o[j][v] = __builtin_fmaf(ga[v], tanh_only(alpha * xr[j].get(v)), be[v]);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+            const int64_t row = base + j * R + grp;
+            if (row < g.M) store12<T>(y + row * g.N + col, o[j]);
+        }
+    }
+}
+
+// Backward stage 1 (PG 0: dx only), one row per lane group and step.  Partial row blockIdx.x:
+// dgamma | dbeta through the LDS combine of the 12-byte LayerNorm backward, dalpha (column 2N)
+// as the workgroup's sum.  With a finite alpha a row past M (x = dy = 0) adds exactly 0; with
+// alpha = +-inf its terms are dropped after the arithmetic, as in the general kernels.
+template <typename T, typename PT, int TPR, int PG>
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256)))
+dyt_bwd_flat12_kernel(const T* __restrict__ x, const T* __restrict__ dy, const PT* __restrict__ alpha_p,
+                      const PT* __restrict__ gamma, T* __restrict__ dx, float* __restrict__ ws, Geom g) {
+    constexpr int V = Words12<T>::V;
+    constexpr int R = 64 / TPR;
+    extern __shared__ float part[];
+    __shared__ float red[kRedFloats];
+    const int wl = threadIdx.x & 63, grp = wl / TPR, lane = wl % TPR;
+    const int wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)lane * V;
+    float ga[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) ga[v] = to_f32(gamma[col + v]);
+    const float alpha = to_f32(alpha_p[0]);
+    const bool finite_alpha = __builtin_isfinite(alpha);
+    float acc_g[V], acc_b[V], acc_a = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc_g[v] = acc_b[v] = 0.f;
+    for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += gridDim.x) {
+        const int64_t row = tile * g.rpp + (int64_t)wave * R + grp;
+        const bool ok = row < g.M;
+        const int64_t lr = ok ? row : g.M - 1;
+        Words12<T> xr, gr;
+        xr.load(x + lr * g.N + col, ok);
+        gr.load(dy + lr * g.N + col, ok);
+        float o[V];
+        if (finite_alpha) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float xv = xr.get(v), gv = gr.get(v);
+                const TanhSech2 ts = tanh_sech2(alpha * xv);
+                const float ds = gv * ga[v] * ts.s;   // dy * gamma * sech^2
+                if constexpr (PG) {
+                    acc_g[v] = __builtin_fmaf(gv, ts.t, acc_g[v]);
+                    acc_b[v] += gv;
+                    acc_a = __builtin_fmaf(xv, ds, acc_a);
+                }
+                o[v] = alpha * ds;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float xv = xr.get(v), gv = gr.get(v);
+                const TanhSech2 ts = tanh_sech2(alpha * xv);
+                const float d = gv * ga[v];
+                const float as = ts.s == 0.f ? 0.f : alpha * ts.s;
+                if constexpr (PG) {
+                    acc_g[v] += ok ? gv * ts.t : 0.f;
+                    acc_b[v] += ok ? gv : 0.f;
+                    acc_a += ok ? d * xv * ts.s : 0.f;
+                }
+                o[v] = d * as;
+            }
+        }
+        if (ok) store12<T>(dx + row * g.N + col, o);
+    }
+    if constexpr (PG != 0) {
+        float* out = ws + blockIdx.x * g.ws_rs;
+        write_partial_pair<T, TPR, 3, V>(out, out + g.N * g.ws_cs, g.ws_cs, acc_g, acc_b, lane, true, col, part);
+        const float da = block_sum(acc_a, red);
+        if (threadIdx.x == 0) out[2 * g.N * g.ws_cs] = da;
+    }
+}
+
 // ============================================================================== RMSNorm
 
 template <typename T, int MODE, int CPT, int RT>

@@ -269,6 +269,11 @@ hipError_t launch_ln_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, co
                               const float* mean, const float* rstd, const void* gamma, float eps,
                               void* dx, float* ws, int grads, hipStream_t s);
 int resident_wgs_ln_flat(bool backward, const Plan& p, int xdt, int pdt);
+hipError_t launch_dyt_fwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* alpha,
+                               const void* gamma, const void* beta, void* y, hipStream_t s);
+hipError_t launch_dyt_bwd_flat(const Plan& p, int xdt, int pdt, const void* x, const void* dy,
+                               const void* alpha, const void* gamma, void* dx, float* ws, hipStream_t s);
+int resident_wgs_dyt_flat(bool backward, const Plan& p, int xdt, int pdt);
 
 hipError_t launch_rms_fwd(const Plan& p, int xdt, int pdt, int variant, const void* x, const void* w,
                           float eps, void* y, float* rstd, hipStream_t s);

@@ -146,9 +146,9 @@ def test_plan_covers_rows_and_columns(M, N, dtype, backward):
                 assert 1 <= gt <= max(p["ntiles"], 1) and (gt >= p["ntiles"] or (gt * p["rpp"]) % V == 0), p
                 continue
             if p["flat"] == 2:
-                # LayerNorm rows of 12 * 2^k bytes in 12-byte chunks: every lane of a row's
+                # LayerNorm / DyT rows of 12 * 2^k bytes in 12-byte chunks: every lane of a row's
                 # power-of-two group live, 4-byte aligned operands, whole waves, a persistent grid
-                assert layer == "layernorm" and mis % 4 == 0 and V == 12 // esz, p
+                assert layer in ("layernorm", "dyt") and mis % 4 == 0 and V == 12 // esz, p
                 assert N * esz == 12 * p["tpr"] and p["tpr"] <= 64 and p["tpr"] & (p["tpr"] - 1) == 0, p
                 assert p["cpt"] == 1 and p["ncb"] == 1 and p["prefetch"] == 0 and p["xcd_remap"] == 0, p
                 assert p["rt"] == (1 if backward or p["tpr"] == 1 else 2), p
@@ -290,9 +290,10 @@ def test_plan_uses_narrow_tiles_for_narrow_rows():
 @pytest.mark.parametrize("backward", [False, True])
 def test_flat_plans(backward):
     """LayerNorm rows of 12 * 2^k bytes (2^k <= 64) on 4-byte aligned operands take the flat
-    kernels with 12-byte chunks (flat 2); other narrow aligned LayerNorm plans with one chunk and
-    one row per thread (group sizes 1..64 lanes, no pipelining, at most 256 threads) take the
-    16-byte flat kernels (flat 1); every other plan, and every other layer, keeps the general
+    kernels with 12-byte chunks (flat 2), and so do such DyT rows in the backward and, where the
+    rows are not whole 16-byte chunks, in the forward; other narrow aligned LayerNorm plans with one
+    chunk and one row per thread (group sizes 1..64 lanes, no pipelining, at most 256 threads)
+    take the 16-byte flat kernels (flat 1); every other plan, and RMSNorm, keeps the general
     kernels."""
     for dtype, V in ((torch.float32, 4), (torch.bfloat16, 8), (torch.float16, 8)):
         esz = 16 // V
@@ -301,7 +302,9 @@ def test_flat_plans(backward):
                 for layer in ("dyt", "layernorm", "rmsnorm"):
                     p = rwn.plan(layer, backward, 4099, N, dtype, misalign_bytes=mis, cus=256)
                     lanes = N * esz // 12
-                    want12 = (layer == "layernorm" and (N * esz) % 12 == 0 and lanes <= 64
+                    whole16 = (N * esz) % 16 == 0 and mis % 16 == 0
+                    want12 = ((layer == "layernorm" or (layer == "dyt" and (backward or not whole16)))
+                              and (N * esz) % 12 == 0 and lanes <= 64
                               and lanes & (lanes - 1) == 0 and mis % 4 == 0)
                     want = (layer == "layernorm" and p["mode"] == 0 and p["cpt"] == 1 and p["rt"] == 1
                             and p["tpr"] <= 64 and p["ncb"] == 1)

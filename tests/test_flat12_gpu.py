@@ -1,4 +1,4 @@
-"""GPU parity of the flat LayerNorm kernels with 12-byte lane chunks (plans with flat = 2): rows
+"""GPU parity of the flat LayerNorm (and DyT) kernels with 12-byte lane chunks (plans with flat = 2): rows
 of 12 * 2^k bytes (float32 N = 3 * 2^k, 16-bit N = 6 * 2^k, 2^k <= 64 lanes per row) on 4-byte
 aligned operands.  Every group size and dtype pair, ragged row counts, row counts that give every
 workgroup several tiles, operands 4 bytes (not 16) past an aligned address, a forward without
@@ -64,6 +64,35 @@ def test_several_tiles_per_workgroup(xdt):
         assert p["ntiles"] >= 2 * p["grid"] and pb["ntiles"] >= 2 * pb["grid"], (p, pb)
         wl = workloads.small("layernorm", M, N, xdt, "f32", seed=lanes)
         _banner(wl, "tiles per workgroup", p["ntiles"] / p["grid"], pb["ntiles"] / pb["grid"])
+        reps += gc.check_workload(wl, DEV)
+    tol.assert_reports(reps)
+
+
+@pytest.mark.parametrize("xdt,pdt", PAIRS)
+def test_dyt_every_group_size_and_ragged_rows(xdt, pdt):
+    """DyT rows of 12 * 2^k bytes take the 12-byte kernels too (backwards always, forwards where
+    the rows are not whole 16-byte chunks): group sizes 1..64 lanes at 1, 63
+    and 1031 rows, then row counts that give every workgroup of both grids several tiles, and
+    alpha = +inf, 0 and negative values (the general kernels' edge handling), against the
+    oracle."""
+    reps = []
+    for N in _widths(xdt):
+        for M in (1, 63, 1031):
+            wl = workloads.small("dyt", M, N, xdt, pdt, seed=N + 11 * M)
+            p, pb = rwn.plan("dyt", False, M, N, gc.DT[xdt], param_dtype=gc.DT[pdt]), rwn.plan("dyt", True, M, N, gc.DT[xdt])
+            esz = 4 if xdt == "f32" else 2
+            assert pb["flat"] == 2 and p["flat"] == (2 if (N * esz) % 16 else 0), (wl.name, p, pb)
+            _banner(wl)
+            reps += gc.check_workload(wl, DEV)
+    esz = 4 if xdt == "f32" else 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for lanes, alpha in ((2, 0.5), (8, float("inf")), (16, 0.0), (64, -1.5)):
+        N = 12 * lanes // esz
+        M = 2 * 8 * cus * 4 * (64 // lanes) * 2 + 29
+        wl = workloads.small("dyt", M, N, xdt, pdt, seed=lanes, alpha=alpha)
+        pb = rwn.plan("dyt", True, M, N, gc.DT[xdt])
+        assert pb["flat"] == 2 and pb["ntiles"] >= 2 * pb["grid"], pb
+        _banner(wl, "alpha", alpha, "tiles per workgroup", pb["ntiles"] / pb["grid"])
         reps += gc.check_workload(wl, DEV)
     tol.assert_reports(reps)
 
