@@ -47,7 +47,9 @@
  *            straddle one more chunk, so those calls take N <= 16381 and otherwise return
  *            RWN_ERR_UNSUPPORTED.  DyT splits wide rows into column blocks and takes every N up
  *            to 16384.  LayerNorm rows of 12 * 2^k bytes (float32 N = 3, 6, ..., 192; 16-bit
- *            N = 6, 12, ..., 384) on 4-byte aligned operands move in 12-byte chunks instead.
+ *            N = 6, 12, ..., 384) on 4-byte aligned operands move in 12-byte chunks instead, and
+ *            so do such DyT rows in the backward (and in the forward where they are not whole
+ *            16-byte chunks).
  */
 #ifndef RWNORM_H
 #define RWNORM_H
@@ -280,8 +282,8 @@ rwn_status rwn_stream_probe(const void* src, const void* src2, void* dst, size_t
  *  (1: workgroup numbers renumbered so consecutive ones share an XCD), prefetch (1: the next
  *  tile's loads are issued before the current tile is processed), flat (1: narrow aligned
  *  LayerNorm rows through plain loads on clamped row indices instead of per-tile buffer
- *  descriptors; 2: the same for LayerNorm rows of 12 * 2^k bytes, 2^k <= 64, on 4-byte aligned
- *  operands, in 12-byte chunks, so elements per chunk is 12 / element size), split (1: a wide row not aligned to 16-byte chunks is cut into whole aligned
+ *  descriptors; 2: the same for LayerNorm and DyT rows of 12 * 2^k bytes, 2^k <= 64, on 4-byte
+ *  aligned operands, in 12-byte chunks, so elements per chunk is 12 / element size), split (1: a wide row not aligned to 16-byte chunks is cut into whole aligned
  *  chunks plus scalar head and tail elements)}.  param_dtype: the parameter
  * dtype of a forward (-1: any; a backward is always planned for every parameter dtype, as its
  * workspace is).  misalign_bytes is the common address of x/y/dy/dx modulo 16.  cus: 0 plans
