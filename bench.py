@@ -340,8 +340,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the path shards across GPUs by rows "
-              "(see the design notes), but no multi-GPU run is part of it. Use --gpus 1.", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; the path shards across GPUs by rows, "
+              "but no multi-GPU run is measured. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads
